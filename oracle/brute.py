@@ -1,0 +1,50 @@
+"""Pure-Python scalar-loop attention for tiny inputs (N <= 16) -- test infrastructure only.
+
+No numpy arithmetic: every sum is ``math.fsum`` (exactly rounded) and every
+exponential is ``math.exp``. It exists to pin ``oracle.attention`` on small
+cases, including the backward, by an independent evaluation order.
+"""
+from __future__ import annotations
+
+import math
+
+
+def _dot(a, b):
+    return math.fsum(x * y for x, y in zip(a, b))
+
+
+def forward(q, k, v, causal, scale):
+    """q, k, v: nested lists [N][D] of floats for one head. Returns (O [N][D], lse [N])."""
+    n = len(q)
+    o, lse = [], []
+    for i in range(n):
+        keys = [j for j in range(len(k)) if not (causal and j > i)]
+        s = [scale * _dot(q[i], k[j]) for j in keys]
+        m = max(s)
+        e = [math.exp(x - m) for x in s]
+        l = math.fsum(e)
+        o.append([math.fsum(e[t] * v[j][d] for t, j in enumerate(keys)) / l for d in range(len(v[0]))])
+        lse.append(m + math.log(l))
+    return o, lse
+
+
+def backward(q, k, v, do, causal, scale):
+    """Loop form of dQ, dK, dV for one head (nested lists)."""
+    n, dd = len(q), len(q[0])
+    nk = len(k)
+    p = []
+    for i in range(n):
+        s = [(-math.inf if (causal and j > i) else scale * _dot(q[i], k[j])) for j in range(nk)]
+        m = max(s)
+        e = [0.0 if x == -math.inf else math.exp(x - m) for x in s]
+        l = math.fsum(e)
+        p.append([x / l for x in e])
+    dp = [[_dot(do[i], v[j]) for j in range(nk)] for i in range(n)]
+    ds = []
+    for i in range(n):
+        c = math.fsum(p[i][j] * dp[i][j] for j in range(nk))
+        ds.append([p[i][j] * (dp[i][j] - c) for j in range(nk)])
+    dv = [[math.fsum(p[i][j] * do[i][d] for i in range(n)) for d in range(len(v[0]))] for j in range(nk)]
+    dq = [[scale * math.fsum(ds[i][j] * k[j][d] for j in range(nk)) for d in range(dd)] for i in range(n)]
+    dk = [[scale * math.fsum(ds[i][j] * q[i][d] for i in range(n)) for d in range(dd)] for j in range(nk)]
+    return dq, dk, dv

@@ -1,0 +1,228 @@
+"""Checks that pin the oracle to facts other than itself.
+
+Each ``pin_*`` function takes the forward and/or backward implementation to
+check (``oracle.attention.forward`` / ``backward`` normally; a deliberately
+broken copy in ``test_oracle_mutations.py``) and raises AssertionError when
+the implementation disagrees with the fact it encodes. The facts come from
+the definition of softmax attention and from calculus, not from the oracle's
+own code:
+
+  * hand-derived worked examples (tests/golden/hand_cases.json);
+  * closed forms: Q = 0 gives the (prefix) mean of V with lse = ln(count);
+    equal key rows give constant scores, lse = c + ln N and O = mean(V);
+    V = 1 gives O = 1 (softmax rows sum to one);
+  * invariances: a shared permutation of K and V rows (non-causal), adding
+    the same vector to every key row (shifts lse by scale*q.u, leaves O),
+    rescaling q by c and scale by 1/c;
+  * torch's CPU float64 scaled_dot_product_attention and autograd of the
+    plain formula (library routines);
+  * central finite differences of the forward for the backward;
+  * exact backward identities: sum_j dK_j = 0, sum_j dV_j = sum_i dO_i, and
+    dQ = dK = 0 when all value rows are equal.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")
+
+_SYMBOLS = {"ln2": math.log(2.0), "ln3": math.log(3.0), "ln4": math.log(4.0)}
+
+
+def _val(x):
+    if isinstance(x, str):
+        return float(eval(x, {"__builtins__": {}}, dict(_SYMBOLS)))  # symbols only
+    return float(x)
+
+
+def _arr(rows):
+    return np.array([[_val(x) for x in r] for r in rows], dtype=np.float64)
+
+
+def load_hand_cases():
+    with open(GOLDEN) as f:
+        return json.load(f)["cases"]
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def pin_hand_cases(fwd, bwd=None, tol=1e-12):
+    for c in load_hand_cases():
+        q, k, v = (_arr(c[n])[None, None] for n in ("q", "k", "v"))
+        o, lse = fwd(q, k, v, c["causal"], c["scale"])
+        np.testing.assert_allclose(o[0, 0], _arr(c["o"]), atol=tol, err_msg=c["name"])
+        np.testing.assert_allclose(lse[0, 0], [_val(x) for x in c["lse"]], atol=tol, err_msg=c["name"])
+        if bwd is not None and "do" in c:
+            do = _arr(c["do"])[None, None]
+            dq, dk, dv = bwd(q, k, v, do, c["causal"], c["scale"])
+            for name, got in (("dq", dq), ("dk", dk), ("dv", dv)):
+                np.testing.assert_allclose(got[0, 0], _arr(c[name]), atol=tol, err_msg=c["name"] + name)
+
+
+def pin_zero_query(fwd, N=37, D=8, tol=1e-12):
+    """Q = 0: every kept score is 0, so weights are uniform over the kept keys."""
+    v = _rand((2, 3, N, D), 1)
+    k = _rand((2, 3, N, D), 2)
+    q = np.zeros((2, 3, N, D))
+    o, lse = fwd(q, k, v, False, 0.3)
+    np.testing.assert_allclose(o, np.broadcast_to(v.mean(axis=2, keepdims=True), o.shape), atol=tol)
+    np.testing.assert_allclose(lse, math.log(N), atol=tol)
+    o, lse = fwd(q, k, v, True, 0.3)
+    counts = np.arange(1, N + 1, dtype=np.float64)
+    prefix_mean = np.cumsum(v, axis=2) / counts[None, None, :, None]
+    np.testing.assert_allclose(o, prefix_mean, atol=tol)
+    np.testing.assert_allclose(lse, np.broadcast_to(np.log(counts), lse.shape), atol=tol)
+
+
+def pin_constant_scores(fwd, N=29, D=16, tol=1e-11):
+    """All key rows equal to u: s_ij = scale q_i.u for every j."""
+    q = _rand((1, 2, N, D), 3)
+    u = _rand((D,), 4)
+    k = np.broadcast_to(u, (1, 2, N, D)).copy()
+    v = _rand((1, 2, N, D), 5)
+    scale = 0.7
+    o, lse = fwd(q, k, v, False, scale)
+    c = scale * (q @ u)
+    np.testing.assert_allclose(lse, c + math.log(N), atol=tol)
+    np.testing.assert_allclose(o, np.broadcast_to(v.mean(axis=2, keepdims=True), o.shape), atol=tol)
+
+
+def pin_ones_value(fwd, N=23, D=4, tol=1e-12):
+    """V = 1: softmax rows sum to one, so every output entry is exactly 1."""
+    q, k = _rand((1, 1, N, D), 6, 3.0), _rand((1, 1, N, D), 7, 3.0)
+    for causal in (False, True):
+        o, _ = fwd(q, k, np.ones((1, 1, N, D)), causal, 1.0)
+        np.testing.assert_allclose(o, 1.0, atol=tol)
+
+
+def pin_permutation(fwd, N=41, D=8, tol=1e-12):
+    """The non-causal result does not depend on the order of the (key, value) pairs."""
+    q, k, v = _rand((1, 2, N, D), 8), _rand((1, 2, N, D), 9), _rand((1, 2, N, 5), 10)
+    perm = np.random.default_rng(11).permutation(N)
+    o1, l1 = fwd(q, k, v, False, 0.4)
+    o2, l2 = fwd(q, k[:, :, perm], v[:, :, perm], False, 0.4)
+    np.testing.assert_allclose(o1, o2, atol=tol)
+    np.testing.assert_allclose(l1, l2, atol=tol)
+
+
+def pin_key_shift(fwd, N=33, D=8, tol=1e-11):
+    """k_j -> k_j + u adds scale q_i.u to every score of row i: O unchanged, lse shifted."""
+    q, k, v = _rand((1, 2, N, D), 12), _rand((1, 2, N, D), 13), _rand((1, 2, N, D), 14)
+    u = _rand((D,), 15, 2.0)
+    scale = 0.6
+    for causal in (False, True):
+        o1, l1 = fwd(q, k, v, causal, scale)
+        o2, l2 = fwd(q, k + u, v, causal, scale)
+        np.testing.assert_allclose(o2, o1, atol=tol)
+        np.testing.assert_allclose(l2, l1 + scale * (q @ u), atol=tol)
+
+
+def pin_scale_fold(fwd, N=19, D=8, tol=1e-12):
+    """(c q) and scale / c give the same scores as q and scale."""
+    q, k, v = _rand((1, 1, N, D), 16), _rand((1, 1, N, D), 17), _rand((1, 1, N, D), 18)
+    for causal in (False, True):
+        o1, l1 = fwd(q, k, v, causal, 0.5)
+        o2, l2 = fwd(2.5 * q, k, v, causal, 0.2)
+        np.testing.assert_allclose(o1, o2, atol=tol)
+        np.testing.assert_allclose(l1, l2, atol=tol)
+
+
+def pin_torch_forward(fwd, tol=1e-12):
+    """torch CPU float64 scaled_dot_product_attention (a library routine) on small shapes."""
+    import torch
+
+    for (B, H, N, D, causal, seed) in [(2, 3, 17, 8, False, 20), (1, 2, 31, 16, True, 21), (1, 1, 5, 64, True, 22)]:
+        q, k, v = (_rand((B, H, N, D), seed + i) for i in range(3))
+        scale = 1.0 / math.sqrt(D) * 1.3
+        o, lse = fwd(q, k, v, causal, scale)
+        tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale)
+        np.testing.assert_allclose(o, ref.numpy(), atol=tol)
+        s = scale * (tq @ tk.transpose(-1, -2))
+        if causal:
+            s = s.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
+        np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy(), atol=tol)
+
+
+def pin_torch_backward(bwd, tol=1e-11):
+    """Autograd (torch CPU float64) of the plain formula sum(dO * softmax(scale QK^T + mask) V)."""
+    import torch
+
+    for (B, H, N, D, causal, seed) in [(1, 2, 13, 8, False, 30), (2, 1, 24, 16, True, 31)]:
+        q, k, v, do = (_rand((B, H, N, D), seed + i) for i in range(4))
+        scale = 0.37
+        dq, dk, dv = bwd(q, k, v, do, causal, scale)
+        tq, tk, tv = (torch.from_numpy(x).requires_grad_(True) for x in (q, k, v))
+        s = scale * (tq @ tk.transpose(-1, -2))
+        if causal:
+            s = s.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
+        o = torch.softmax(s, dim=-1) @ tv
+        (o * torch.from_numpy(do)).sum().backward()
+        for got, t in ((dq, tq), (dk, tk), (dv, tv)):
+            np.testing.assert_allclose(got, t.grad.numpy(), atol=tol)
+
+
+def pin_finite_differences(fwd, bwd, tol=1e-7):
+    """Central differences of L = sum(dO * O) against the analytic gradients (N, D <= 8)."""
+    for (N, D, causal, seed) in [(6, 4, False, 40), (8, 3, True, 41)]:
+        q, k, v, do = (_rand((1, 1, N, D), seed + i) for i in range(4))
+        scale = 0.8
+        dq, dk, dv = bwd(q, k, v, do, causal, scale)
+        h = 1e-5
+
+        def loss(q_, k_, v_):
+            return float((fwd(q_, k_, v_, causal, scale)[0] * do).sum())
+
+        for which, grad in ((0, dq), (1, dk), (2, dv)):
+            fd = np.zeros_like(grad)
+            for idx in np.ndindex(*q.shape):
+                args = [q.copy(), k.copy(), v.copy()]
+                args[which][idx] += h
+                lp = loss(*args)
+                args[which][idx] -= 2 * h
+                lm = loss(*args)
+                fd[idx] = (lp - lm) / (2 * h)
+            np.testing.assert_allclose(grad, fd, atol=tol)
+
+
+def pin_backward_identities(bwd, N=45, D=8, tol=1e-12):
+    """Identities of the exact gradient, for any inputs."""
+    q, k, v, do = (_rand((1, 2, N, D), 50 + i) for i in range(4))
+    for causal in (False, True):
+        dq, dk, dv = bwd(q, k, v, do, causal, 0.45)
+        # rows of dS sum to zero => sum_j dK_j = scale * sum_i (sum_j dS_ij) q_i = 0
+        np.testing.assert_allclose(dk.sum(axis=2), 0.0, atol=tol)
+        # rows of P sum to one => sum_j dV_j = sum_i dO_i
+        np.testing.assert_allclose(dv.sum(axis=2), do.sum(axis=2), atol=tol)
+    # all value rows equal => O is constant in Q and K => dQ = dK = 0
+    v_eq = np.broadcast_to(_rand((D,), 60), q.shape).copy()
+    for causal in (False, True):
+        dq, dk, _ = bwd(q, k, v_eq, do, causal, 0.45)
+        np.testing.assert_allclose(dq, 0.0, atol=tol)
+        np.testing.assert_allclose(dk, 0.0, atol=tol)
+
+
+def pin_brute_force(fwd, bwd, brute, tol=1e-12):
+    """Pure-Python loops (math.fsum / math.exp) on N <= 16."""
+    for (N, D, causal, seed) in [(1, 3, False, 70), (7, 5, True, 71), (16, 8, False, 72), (16, 4, True, 73)]:
+        q, k, v, do = (_rand((1, 1, N, D), seed + i) for i in range(4))
+        scale = 0.9
+        o, lse = fwd(q, k, v, causal, scale)
+        bo, blse = brute.forward(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), causal, scale)
+        np.testing.assert_allclose(o[0, 0], np.array(bo), atol=tol)
+        np.testing.assert_allclose(lse[0, 0], np.array(blse), atol=tol)
+        if bwd is not None:
+            g = bwd(q, k, v, do, causal, scale)
+            bg = brute.backward(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), do[0, 0].tolist(), causal, scale)
+            for got, ref in zip(g, bg):
+                np.testing.assert_allclose(got[0, 0], np.array(ref), atol=tol)
+
+
+FORWARD_PINS = [pin_zero_query, pin_constant_scores, pin_ones_value, pin_permutation, pin_key_shift,
+                pin_scale_fold, pin_torch_forward]

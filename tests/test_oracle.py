@@ -1,0 +1,51 @@
+"""The oracle against its pins (CPU only)."""
+import numpy as np
+import pytest
+
+import oracle_pins as pins
+from oracle import attention, brute
+
+
+def test_hand_cases():
+    pins.pin_hand_cases(attention.forward, attention.backward)
+
+
+@pytest.mark.parametrize("pin", pins.FORWARD_PINS, ids=lambda p: p.__name__)
+def test_forward_pin(pin):
+    pin(attention.forward)
+
+
+def test_torch_backward():
+    pins.pin_torch_backward(attention.backward)
+
+
+def test_finite_differences():
+    pins.pin_finite_differences(attention.forward, attention.backward)
+
+
+def test_backward_identities():
+    pins.pin_backward_identities(attention.backward)
+
+
+def test_brute_force():
+    pins.pin_brute_force(attention.forward, attention.backward, brute)
+
+
+def test_softmax_rows_sum_to_one():
+    s = np.random.default_rng(0).standard_normal((64, 300)) * 10
+    s[:, 7] = -np.inf
+    p, lse = attention.softmax_rows(s)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=1e-14)
+    assert (p[:, 7] == 0).all()
+    np.testing.assert_allclose(lse, np.log(np.exp(np.where(np.isinf(s), -np.inf, s)).sum(axis=1)), rtol=1e-13)
+
+
+def test_row_subset_matches_full():
+    rng = np.random.default_rng(1)
+    q, k, v = (rng.standard_normal((2, 2, 300, 8)) for _ in range(3))
+    rows = np.array([0, 1, 5, 100, 299])
+    for causal in (False, True):
+        o, lse = attention.forward(q, k, v, causal, 0.35)
+        o_s, lse_s = attention.forward(q, k, v, causal, 0.35, rows=rows)
+        np.testing.assert_allclose(o_s, o[:, :, rows], atol=1e-14)
+        np.testing.assert_allclose(lse_s, lse[:, :, rows], atol=1e-14)

@@ -1,0 +1,116 @@
+"""Plausible mistakes planted in copies of the oracle (on the CPU) must each fail a pin.
+
+This shows the pins are sharp enough to catch a dropped term, a wrong sign,
+a wrong index or a transposed operand anywhere in the oracle.
+"""
+import numpy as np
+import pytest
+
+import oracle_pins as pins
+from oracle import attention, brute
+
+
+def _fwd_factory(mask_shift=0, scale_pow=1, use_max=True, lse_log=np.log, transpose_k=False, v_t=False):
+    def fwd(q, k, v, causal, scale, rows=None):
+        q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+        B, H, N, D = q.shape
+        o = np.empty((B, H, N, v.shape[-1]))
+        lse = np.empty((B, H, N))
+        for b in range(B):
+            for h in range(H):
+                kk = k[b, h][::-1] if transpose_k else k[b, h]
+                s = (scale ** scale_pow) * (q[b, h] @ kk.T)
+                if causal:
+                    s = np.where(np.arange(N)[None, :] > np.arange(N)[:, None] + mask_shift, -np.inf, s)
+                m = s.max(axis=1) if use_max else np.zeros(N)
+                p = np.exp(s - m[:, None])
+                l = p.sum(axis=1)
+                vv = v[b, h][::-1] if v_t else v[b, h]
+                o[b, h] = (p @ vv) / l[:, None]
+                lse[b, h] = (m if use_max else 0) + lse_log(l)
+        return o, lse
+    return fwd
+
+
+FORWARD_MUTANTS = {
+    "mask_off_by_one": _fwd_factory(mask_shift=1),
+    "mask_excludes_diagonal": _fwd_factory(mask_shift=-1),
+    "scale_squared": _fwd_factory(scale_pow=2),
+    "lse_log2": _fwd_factory(lse_log=np.log2),
+    "keys_reversed": _fwd_factory(transpose_k=True),
+    "values_reversed": _fwd_factory(v_t=True),
+}
+
+
+def _all_forward_pins(fwd):
+    failures = 0
+    for pin in pins.FORWARD_PINS:
+        try:
+            pin(fwd)
+        except AssertionError:
+            failures += 1
+    try:
+        pins.pin_hand_cases(fwd)
+    except AssertionError:
+        failures += 1
+    return failures
+
+
+def test_unmutated_forward_passes_every_pin():
+    assert _all_forward_pins(attention.forward) == 0
+
+
+@pytest.mark.parametrize("name", sorted(FORWARD_MUTANTS))
+def test_forward_mutant_is_caught(name):
+    assert _all_forward_pins(FORWARD_MUTANTS[name]) > 0, name
+
+
+def _bwd_factory(drop_jacobian_term=False, sign=1.0, dk_from_k=False, dv_untransposed=False, no_scale=False):
+    def bwd(q, k, v, do, causal, scale):
+        q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+        dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+        B, H, N, D = q.shape
+        for b in range(B):
+            for h in range(H):
+                s = attention.scores(q[b, h], k[b, h], scale, causal)
+                p, _ = attention.softmax_rows(s)
+                dv[b, h] = (p if dv_untransposed else p.T) @ do[b, h]
+                dp = do[b, h] @ v[b, h].T
+                c = 0.0 if drop_jacobian_term else (p * dp).sum(axis=1, keepdims=True)
+                ds = p * (dp - sign * c)
+                f = 1.0 if no_scale else scale
+                dq[b, h] = f * (ds @ k[b, h])
+                dk[b, h] = f * (ds.T @ (k[b, h] if dk_from_k else q[b, h]))
+        return dq, dk, dv
+    return bwd
+
+
+BACKWARD_MUTANTS = {
+    "drop_jacobian_term": _bwd_factory(drop_jacobian_term=True),
+    "jacobian_sign": _bwd_factory(sign=-1.0),
+    "dk_uses_k": _bwd_factory(dk_from_k=True),
+    "dv_untransposed": _bwd_factory(dv_untransposed=True),
+    "missing_scale": _bwd_factory(no_scale=True),
+}
+
+
+def _all_backward_pins(bwd):
+    failures = 0
+    for f in (lambda: pins.pin_hand_cases(attention.forward, bwd),
+              lambda: pins.pin_backward_identities(bwd),
+              lambda: pins.pin_finite_differences(attention.forward, bwd),
+              lambda: pins.pin_torch_backward(bwd)):
+        try:
+            f()
+        except AssertionError:
+            failures += 1
+    return failures
+
+
+@pytest.mark.parametrize("name", sorted(BACKWARD_MUTANTS))
+def test_backward_mutant_is_caught(name):
+    assert _all_backward_pins(BACKWARD_MUTANTS[name]) > 0, name
+
+
+def test_unmutated_backward_passes_every_pin():
+    assert _all_backward_pins(attention.backward) == 0

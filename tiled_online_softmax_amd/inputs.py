@@ -1,0 +1,120 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the bench.
+
+This module draws random numbers and encodes them as the storage types the
+kernels read (fp32, or bf16 bit patterns). It holds none of the attention
+arithmetic and none of the FP8 quantisation recipe: those live, separately,
+in the HIP library and in the oracle.
+
+Recipe (the same everywhere):
+  * generator: numpy ``default_rng(seed)`` (PCG64), ``standard_normal`` in
+    float32, drawn in the order Q, K, V, dO, each of shape [B, H, N, D];
+  * an optional multiplier (0.5 for the large-head-dim workload) is applied
+    in float32, which is exact for a power of two;
+  * bf16 inputs are the round-to-nearest-even bf16 of those float32 values.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Optional
+
+import numpy as np
+
+SEED_BASE = 20261203
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One attention problem: shapes, storage type and masking."""
+
+    name: str
+    B: int
+    H: int
+    N: int
+    D: int
+    dtype: str  # "f32", "bf16" or "fp8" (fp8: e4m3 codes quantised from f32 draws)
+    causal: bool
+    passes: str  # "fwd" or "bwd"
+    multiplier: float = 1.0
+    seed: int = SEED_BASE
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.D))
+
+    @property
+    def shape(self):
+        return (self.B, self.H, self.N, self.D)
+
+    def fwd_flops(self) -> float:
+        """Two N x N x D contractions (QK^T and PV), 2 flops per FMA; causal is half."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.D
+        return f / 2 if self.causal else f
+
+    def bwd_flops(self) -> float:
+        """Five N x N x D contractions (S, dV, dP, dQ, dK); causal is half."""
+        f = 10.0 * self.B * self.H * self.N * self.N * self.D
+        return f / 2 if self.causal else f
+
+
+# The five workloads the library is specified and measured on.
+WORKLOADS: Dict[str, Workload] = {
+    "single_head_f32": Workload("single_head_f32", 1, 1, 256, 64, "f32", False, "fwd", seed=SEED_BASE + 1),
+    "mh_causal_bf16": Workload("mh_causal_bf16", 4, 16, 2048, 128, "bf16", True, "fwd", seed=SEED_BASE + 2),
+    "d256_bf16": Workload("d256_bf16", 1, 8, 8192, 256, "bf16", False, "fwd", multiplier=0.5, seed=SEED_BASE + 3),
+    "bwd_causal_bf16": Workload("bwd_causal_bf16", 2, 16, 4096, 64, "bf16", True, "bwd", seed=SEED_BASE + 4),
+    "long_fp8_causal": Workload("long_fp8_causal", 1, 32, 32768, 128, "fp8", True, "fwd", seed=SEED_BASE + 5),
+}
+
+
+def draw(shape, seed: int, count: int = 3, multiplier: float = 1.0):
+    """Return ``count`` float32 arrays of ``shape`` (Q, K, V[, dO]) from one PCG64 stream."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        x = rng.standard_normal(size=shape, dtype=np.float32)
+        if multiplier != 1.0:
+            x = x * np.float32(multiplier)
+        out.append(x)
+    return out
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bf16 (nearest, ties to even); returns the uint16 bit patterns.
+
+    Inputs here are finite normal draws, so no NaN handling is needed; a NaN
+    input raises rather than being silently encoded.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if not np.isfinite(x).all():
+        raise ValueError("f32_to_bf16_bits: non-finite input")
+    u = x.view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to float32 (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def make(w: Workload, with_grad: Optional[bool] = None, seed: Optional[int] = None, shape=None):
+    """Draw the inputs of workload ``w``.
+
+    Returns a dict with float32 draws ``q, k, v`` (and ``do`` for backward
+    workloads) and, for bf16 workloads, the bf16 bit patterns ``q_bits`` etc.
+    ``shape`` overrides the workload's [B, H, N, D] (used for reduced-size
+    parity cases that keep the same value distribution).
+    """
+    if with_grad is None:
+        with_grad = w.passes == "bwd"
+    shp = tuple(shape) if shape is not None else w.shape
+    arrs = draw(shp, w.seed if seed is None else seed, 4 if with_grad else 3, w.multiplier)
+    names = ["q", "k", "v", "do"][: len(arrs)]
+    out = dict(zip(names, arrs))
+    if w.dtype == "bf16":
+        for n in names:
+            out[n + "_bits"] = f32_to_bf16_bits(out[n])
+    elif with_grad:
+        # Gradients of the low-precision paths are taken at bf16 dO.
+        out["do_bits"] = f32_to_bf16_bits(out["do"])
+    return out
