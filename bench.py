@@ -1,0 +1,232 @@
+"""Throughput of the attention hot path on one MI355X.
+
+A step is one pass of the whole path over the multi-head causal workload
+(B=4, H=16, N=2048, D=128, bf16 Q/K/V iid N(0,1), scale 1/sqrt(128)): the
+forward (O and lse) followed by the backward (dQ, dK, dV from the forward's O
+and lse, deterministic variant). `value` is the step's algorithmic TFLOP/s:
+forward 4*B*H*N^2*D plus backward 10*B*H*N^2*D, both halved for causal.
+
+Also reported, each timed on its own with HIP events on the launch stream:
+every other workload's headline pass (the float32 single head, the D=256
+forward, the causal backward, the long-context FP8 forward), the roofline of
+the dominant kernel, and the float64 oracle timed on the host cores on a
+bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-breakdown]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "f32": 157.3}  # MI355X dense MFMA peaks
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-breakdown", action="store_true")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def device_inputs(w, with_grad, shape=None):
+    import torch
+
+    from tiled_online_softmax_amd import inputs
+
+    d = inputs.make(w, with_grad=with_grad, shape=shape)
+    out = {}
+    for n in ("q", "k", "v", "do"):
+        if n not in d:
+            continue
+        if w.dtype == "f32":
+            out[n] = torch.from_numpy(d[n]).to("cuda:0")
+        elif w.dtype == "bf16":
+            out[n] = torch.from_numpy(d[n + "_bits"].view(np.int16)).view(torch.bfloat16).to("cuda:0")
+        else:
+            out[n] = torch.from_numpy(d[n]).to("cuda:0")  # fp32 draws, quantised on the GPU
+    return out
+
+
+def time_fn(fn, iters, warmup=3):
+    """Average milliseconds per call of `fn` (launches on torch's current stream), by HIP events."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def breakdown():
+    """Each workload's headline pass, timed alone."""
+    import torch
+
+    from tiled_online_softmax_amd import fa, inputs
+
+    res = {}
+    for name, w in inputs.WORKLOADS.items():
+        t0 = time.time()
+        x = device_inputs(w, with_grad=(w.passes == "bwd"))
+        if w.dtype == "fp8":
+            qc, qd = fa.quantize_fp8(x["q"])
+            kc, kd = fa.quantize_fp8(x["k"])
+            vc, vd = fa.quantize_fp8(x["v"])
+            del x
+            fn = lambda: fa.fwd_fp8(qc, kc, vc, causal=w.causal, q_descale=qd, k_descale=kd, v_descale=vd)
+            flops, peak, iters = w.fwd_flops(), PEAK_TFLOPS["fp8"], 10
+        elif w.passes == "fwd":
+            fn = lambda: fa.fwd(x["q"], x["k"], x["v"], causal=w.causal)
+            flops = w.fwd_flops()
+            peak = PEAK_TFLOPS["f32" if w.dtype == "f32" else "bf16"]
+            iters = 200 if w.N <= 2048 else 30
+        else:
+            o, lse = fa.fwd(x["q"], x["k"], x["v"], causal=w.causal)
+            ws = torch.empty(fa.bwd_workspace_size(w.B, w.H, w.N, w.D, fa.FA_BWD_DETERMINISTIC), dtype=torch.uint8,
+                             device="cuda:0")
+            fn = lambda: fa.bwd(x["q"], x["k"], x["v"], o, x["do"], lse, causal=w.causal,
+                                variant=fa.FA_BWD_DETERMINISTIC, workspace=ws)
+            flops, peak, iters = w.bwd_flops(), PEAK_TFLOPS["bf16"], 50
+        try:
+            ms = time_fn(fn, iters)
+        except Exception as e:  # report, do not hide
+            res[name] = {"error": str(e)}
+            continue
+        tf = flops / (ms * 1e-3) / 1e12
+        res[name] = {"pass": w.passes, "dtype": w.dtype, "ms": round(ms, 4), "tflops": round(tf, 2),
+                     "pct_of_peak": round(100 * tf / peak, 2), "peak_tflops": peak}
+        log(f"[breakdown] {name}: {ms:.4f} ms  {tf:.1f} TFLOP/s  ({100 * tf / peak:.1f}% of {peak})"
+            f"  [{time.time() - t0:.1f}s]")
+        torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(w, step_flops):
+    """The float64 oracle on a bounded sample (2 heads, forward + backward), scaled to TFLOP/s."""
+    from oracle import attention, codecs
+    from tiled_online_softmax_amd import inputs
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    heads = 2
+    d = inputs.make(w, with_grad=True, shape=(1, heads, w.N, w.D))
+    q, k, v, do = (codecs.bf16_to_f64(d[n + "_bits"]) for n in ("q", "k", "v", "do"))
+    t0 = time.perf_counter()
+    attention.forward(q, k, v, w.causal, w.scale)
+    attention.backward(q, k, v, do, w.causal, w.scale)
+    dt = time.perf_counter() - t0
+    frac = heads / (w.B * w.H)
+    tf = step_flops * frac / dt / 1e12
+    return {"value": round(tf, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.H} (b,h) heads of the step workload, forward + backward, float64 "
+                      f"numpy oracle, {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from tiled_online_softmax_amd import fa, inputs
+
+    fa.lib()
+    w = inputs.WORKLOADS["mh_causal_bf16"]
+    x = device_inputs(w, with_grad=True)
+    variant = fa.FA_BWD_DETERMINISTIC
+    ws = torch.empty(fa.bwd_workspace_size(w.B, w.H, w.N, w.D, variant), dtype=torch.uint8, device="cuda:0")
+    o = torch.empty_like(x["q"])
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda:0")
+    dq, dk, dv = (torch.empty_like(x["q"]) for _ in range(3))
+
+    def fwd():
+        fa.fwd(x["q"], x["k"], x["v"], causal=w.causal, out=o, lse=lse)
+
+    def bwd():
+        fa.bwd(x["q"], x["k"], x["v"], o, x["do"], lse, causal=w.causal, variant=variant, workspace=ws,
+               dq=dq, dk=dk, dv=dv)
+
+    def step():
+        fwd()
+        bwd()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    step_flops = w.fwd_flops() + w.bwd_flops()
+    value = step_flops / (ms * 1e-3) / 1e12
+    log(f"[step] {ms:.4f} ms/step, {value:.1f} TFLOP/s")
+
+    # dominant kernel: time forward and backward launches separately
+    ms_f = time_fn(fwd, 100)
+    ms_b = time_fn(bwd, 100)
+    fwd_tf = w.fwd_flops() / (ms_f * 1e-3) / 1e12
+    bwd_tf = w.bwd_flops() / (ms_b * 1e-3) / 1e12
+    log(f"[fwd] {ms_f:.4f} ms {fwd_tf:.1f} TF/s   [bwd] {ms_b:.4f} ms {bwd_tf:.1f} TF/s")
+    if ms_b >= ms_f:
+        dom = {"kernel": "backward (fa_bwd, deterministic: delta + dK/dV + dQ kernels)", "ms": ms_b, "tf": bwd_tf,
+               "flops": w.bwd_flops()}
+    else:
+        dom = {"kernel": "fa_fwd kernel", "ms": ms_f, "tf": fwd_tf, "flops": w.fwd_flops()}
+    roofline = {"bound": "mfma", "achieved": round(dom["tf"], 2), "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+                "frac": round(dom["tf"] / PEAK_TFLOPS["bf16"], 4), "traffic": None, "kernel": dom["kernel"],
+                "avg_launch_ms": round(dom["ms"], 5), "algorithmic_flops_per_launch": dom["flops"]}
+
+    out = {"metric": "attention fwd/bwd TFLOP/s on 1 MI355X + % of bf16/fp8 MFMA peak", "value": round(value, 2),
+           "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "multi-head causal attention forward + backward", "B": w.B, "H": w.H, "N": w.N,
+                      "D": w.D, "causal": True, "inputs": "bf16 iid N(0,1)", "scale": "1/sqrt(128)",
+                      "bwd_variant": "deterministic"},
+           "pct_of_bf16_peak": round(100 * value / PEAK_TFLOPS["bf16"], 2),
+           "fwd": {"ms": round(ms_f, 5), "tflops": round(fwd_tf, 2)},
+           "bwd": {"ms": round(ms_b, 5), "tflops": round(bwd_tf, 2)},
+           "roofline": roofline}
+    del x
+    torch.cuda.empty_cache()
+    if not args.no_breakdown:
+        out["workloads"] = breakdown()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, step_flops)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

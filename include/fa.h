@@ -1,0 +1,167 @@
+/*
+ * libfa -- exact FlashAttention-style attention for AMD MI355X (gfx950).
+ *
+ * The operation. For each batch b and head h, with q_i, k_j, v_j the rows of
+ * Q, K, V ([N, D] slices of [B, H, N, D] tensors):
+ *     s_ij  = scale * <q_i, k_j>             (causal: only keys j <= i are kept)
+ *     O_i   = sum_j softmax_j(s_ij) v_j
+ *     lse_i = ln sum_j exp(s_ij)              (natural log)
+ * computed without materialising the N x N score matrix: K/V are walked in
+ * tiles, a running row max and sum are kept, and the output is normalised
+ * once at the end. The pages describe this as the "tiled online softmax"
+ * baseline (page "r/mlscaling", FA1 bullet), with query-tile ownership and
+ * deferred normalisation (FA2 bullet), ping-pong tile buffers and an FP8
+ * forward (FA3 bullet), and conditional rescaling (FA4 bullet), all keeping
+ * the same exact attention math (closing sentence of that list). The backward
+ * recomputes the probabilities from lse instead of storing them; the pages
+ * name both the atomics-based backward of FlashAttention-2 and an
+ * atomics-free alternative that spends more matrix multiplies ("FlashAttention
+ * (Metal Port)" README, section "Documentation").
+ *
+ * Layout: Q, K, V, O, dO, dQ, dK, dV are contiguous row-major [B, H, N, D];
+ * lse is contiguous float32 [B, H, N]. Query and key lengths are equal.
+ *
+ * Ownership: the caller allocates and owns every buffer (device memory).
+ * The library never allocates, frees or synchronises, and keeps no state
+ * except a per-thread error string. Every call is asynchronous on `stream`
+ * (a hipStream_t passed as void*; NULL is the default stream). Device-side
+ * faults surface at the caller's next synchronisation, as with any HIP call.
+ *
+ * Errors: every entry point returns an fa_status. Arguments are validated
+ * before any HIP call (so validation works without a GPU); on failure
+ * fa_last_error() describes the problem. FA_ERR_INVALID_ARG: null pointer,
+ * B/H/N/D < 1, scale negative or not finite, causal not 0/1, a pointer not
+ * 16-byte aligned, or one head larger than 2^31 bytes. FA_ERR_UNSUPPORTED: D
+ * not in the parameter table or a dtype/pass pair that is not built.
+ * FA_ERR_WORKSPACE: workspace too small. FA_ERR_HIP: a HIP launch error
+ * (hipGetErrorString text in fa_last_error()).
+ */
+#ifndef LIBFA_FA_H
+#define LIBFA_FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FA_F32 = 0, FA_BF16 = 1, FA_FP8_E4M3 = 2 } fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1,
+  FA_ERR_UNSUPPORTED = 2,
+  FA_ERR_WORKSPACE = 3,
+  FA_ERR_HIP = 4
+} fa_status;
+
+/* Backward variants (see fa_bwd). */
+enum { FA_BWD_ATOMIC = 0, FA_BWD_DETERMINISTIC = 1 };
+
+/*
+ * Forward pass.
+ *   q, k, v : [B, H, N, D] of `dtype` (FA_F32: float; FA_BF16: bfloat16;
+ *             FA_FP8_E4M3: OCP e4m3 codes with unit scales -- use
+ *             fa_fwd_fp8 for per-tensor scales).
+ *   o       : [B, H, N, D] output; float for FA_F32, bfloat16 otherwise.
+ *   lse     : [B, H, N] float output, natural-log logsumexp of the scaled
+ *             scores of each query row (what fa_bwd consumes).
+ *   D       : head dimension; FA_F32 and FA_BF16 support 64, 128 and 256,
+ *             FA_FP8_E4M3 supports 64 and 128.
+ *   causal  : 1 keeps key j only for query i >= j.
+ *   scale   : factor on q.k, >= 0 and finite (usually 1/sqrt(D)).
+ * Rows are rescaled when their running max grows by more than 8 in base-2
+ * units (FA_FP8_E4M3: whenever it grows), which is exact in exact arithmetic.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int D, int causal, float scale, int dtype,
+           void* stream);
+
+/*
+ * fa_fwd with an explicit conditional-rescale threshold `rescale_log2`
+ * (>= 0, in base-2 units of the score): a row's reference max is moved --
+ * and its accumulator rescaled -- only when a new tile's max exceeds it by
+ * more than this. 0 rescales on every increase. Ignored (forced to 0) for
+ * FA_FP8_E4M3, whose probabilities must stay <= 1 to fit the e4m3 range.
+ * The result is the same attention for every threshold (the conditional
+ * rescaling of page "r/mlscaling", FA4 bullet, and of the FlashAttention-4
+ * entry on the page "FlashAttention" entity trail, section "Corpus findings").
+ */
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int H, int N, int D, int causal, float scale, int dtype,
+              float rescale_log2, void* stream);
+
+/*
+ * FP8 forward with per-tensor scales (page "r/mlscaling", FA3 bullet names an
+ * FP8 forward path; the scaling recipe is per-tensor amax, see
+ * fa_quantize_fp8).
+ *   q, k, v  : [B, H, N, D] e4m3 codes; the value of an element is
+ *              decode(code) * descale of its tensor.
+ *   q_descale, k_descale, v_descale : device pointers to one float each, or
+ *              NULL for 1.0 (read by the kernel, so they may be produced by
+ *              fa_quantize_fp8 on the same stream without a host sync).
+ *   o        : [B, H, N, D] bfloat16; lse: [B, H, N] float.
+ *   D        : 64 or 128.
+ * Scores use fp8 MFMA with the descales folded into the score scale; the
+ * probabilities are encoded as e4m3(p * 448) for the P.V product while the
+ * row sums and lse use the unencoded float32 p.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int D, int causal, float scale,
+               const float* q_descale, const float* k_descale,
+               const float* v_descale, void* stream);
+
+/*
+ * Per-tensor FP8 quantisation (the operand preparation of the FP8 forward):
+ *   amax    = max |x_i| over all n elements,
+ *   codes_i = e4m3 round-to-nearest-even of x_i * (448 / amax) (float32
+ *             product, saturating at +-448),
+ *   *descale = amax / 448 (1 when amax is 0).
+ *   x       : n floats (device); codes: n bytes (device); descale: one float
+ *             (device) which is also used as the amax accumulator.
+ * Three kernels on `stream`; n >= 1 and n < 2^40.
+ */
+int fa_quantize_fp8(const float* x, size_t n, void* codes, float* descale,
+                    void* stream);
+
+/*
+ * Workspace bytes fa_bwd needs: float D_i = sum_d dO_id O_id [B, H, N], plus a
+ * float dQ accumulator [B, H, N, D] for FA_BWD_ATOMIC. 0 on invalid input.
+ */
+size_t fa_bwd_workspace_size(int B, int H, int N, int D, int dtype, int variant);
+
+/*
+ * Backward pass: gradients of sum(dO * O) with respect to Q, K, V, with the
+ * probabilities recomputed from lse (P = exp(s - lse)) rather than stored.
+ *   q, k, v, o, dO : [B, H, N, D] bfloat16 (dtype must be FA_BF16); o and lse
+ *                    are what fa_fwd returned for the same q, k, v.
+ *   lse            : [B, H, N] float.
+ *   dq, dk, dv     : [B, H, N, D] bfloat16 outputs.
+ *   D              : 64 or 128.
+ *   variant        : FA_BWD_ATOMIC -- one pass over key tiles computing dK, dV
+ *                    and accumulating dQ with float atomics in the workspace
+ *                    (the FlashAttention-2 scheme with scratch for atomics);
+ *                    FA_BWD_DETERMINISTIC -- dK/dV over key tiles plus a
+ *                    separate pass over query tiles for dQ that recomputes
+ *                    the scores (7 matrix products instead of 5, no atomics,
+ *                    bitwise reproducible), as in the "FlashAttention (Metal
+ *                    Port)" README, section "Documentation".
+ *   workspace      : device buffer of at least fa_bwd_workspace_size bytes,
+ *                    16-byte aligned; the library initialises what it needs.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const void* dO, const float* lse, void* dq, void* dk, void* dv,
+           int B, int H, int N, int D, int causal, float scale, int dtype,
+           int variant, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* fa_status_string(int status);
+
+/* Message for the last non-OK return on the calling thread ("" if none). */
+const char* fa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBFA_FA_H */

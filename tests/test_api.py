@@ -1,0 +1,140 @@
+"""The C ABI without a GPU: the library loads, exports what include/fa.h declares, and validates arguments.
+
+Only calls that must fail validation are made here (validation runs before
+any HIP call), with dummy but aligned pointer values that are never
+dereferenced.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from tiled_online_softmax_amd import fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+P = 0x10000  # aligned dummy pointer, never dereferenced (validation fails first)
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "fa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = header_functions()
+    assert set(names) == set(fa.EXPORTED), names
+    L = fa.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    assert fa.status_string(fa.FA_OK) == "FA_OK"
+    assert fa.status_string(fa.FA_ERR_WORKSPACE) == "FA_ERR_WORKSPACE"
+    assert fa.status_string(99) == "FA_UNKNOWN_STATUS"
+
+
+def _fwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=16, D=64, causal=0, scale=0.125, dtype=fa.FA_BF16)
+    a.update(kw)
+    return fa.lib().fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["D"], a["causal"],
+                           a["scale"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(q=None), fa.FA_ERR_INVALID_ARG, "NULL"),
+    (dict(lse=0), fa.FA_ERR_INVALID_ARG, "NULL"),
+    (dict(v=P + 8), fa.FA_ERR_INVALID_ARG, "aligned"),
+    (dict(N=0), fa.FA_ERR_INVALID_ARG, ">= 1"),
+    (dict(B=-1), fa.FA_ERR_INVALID_ARG, ">= 1"),
+    (dict(D=0), fa.FA_ERR_INVALID_ARG, ">= 1"),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG, "causal"),
+    (dict(scale=math.nan), fa.FA_ERR_INVALID_ARG, "scale"),
+    (dict(scale=math.inf), fa.FA_ERR_INVALID_ARG, "scale"),
+    (dict(scale=-1.0), fa.FA_ERR_INVALID_ARG, "scale"),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG, "scale"),
+    (dict(dtype=7), fa.FA_ERR_INVALID_ARG, "dtype"),
+    (dict(D=96), fa.FA_ERR_UNSUPPORTED, "D=96"),
+    (dict(D=256, dtype=fa.FA_FP8_E4M3), fa.FA_ERR_UNSUPPORTED, "D=256"),
+    (dict(N=1 << 24, D=128), fa.FA_ERR_INVALID_ARG, "2^31"),
+])
+def test_fwd_validation(kw, status, msg):
+    assert _fwd(**kw) == status
+    assert msg in fa.last_error()
+
+
+def test_fwd_ex_threshold_validation():
+    L = fa.lib()
+    for bad in (-1.0, math.nan, math.inf):
+        assert L.fa_fwd_ex(P, P, P, P, P, 1, 1, 16, 64, 0, 0.1, fa.FA_BF16, bad, None) == fa.FA_ERR_INVALID_ARG
+        assert "threshold" in fa.last_error()
+
+
+def test_fwd_fp8_validation():
+    L = fa.lib()
+    assert L.fa_fwd_fp8(P, P, P, P, P, 1, 1, 16, 128, 0, 0.1, P + 2, None, None, None) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_fwd_fp8(P, P, P, P, P, 1, 1, 16, 256, 0, 0.1, None, None, None, None) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_quantize_validation():
+    L = fa.lib()
+    assert L.fa_quantize_fp8(P, 0, P, P, None) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_quantize_fp8(None, 10, P, P, None) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_quantize_fp8(P, 10, P, None, None) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_quantize_fp8(P, 10, P, P + 1, None) == fa.FA_ERR_INVALID_ARG
+
+
+def test_workspace_size():
+    L = fa.lib()
+    B, H, N, D = 2, 3, 100, 64
+    det = L.fa_bwd_workspace_size(B, H, N, D, fa.FA_BF16, fa.FA_BWD_DETERMINISTIC)
+    atom = L.fa_bwd_workspace_size(B, H, N, D, fa.FA_BF16, fa.FA_BWD_ATOMIC)
+    assert det >= B * H * N * 4 and det % 256 == 0
+    assert atom == det + B * H * N * D * 4
+    assert L.fa_bwd_workspace_size(B, H, N, D, fa.FA_F32, 0) == 0
+    assert L.fa_bwd_workspace_size(0, H, N, D, fa.FA_BF16, 0) == 0
+    assert L.fa_bwd_workspace_size(B, H, N, D, fa.FA_BF16, 5) == 0
+
+
+def _bwd(**kw):
+    a = dict(B=1, H=1, N=16, D=64, causal=0, scale=0.125, dtype=fa.FA_BF16, variant=fa.FA_BWD_ATOMIC,
+             ws=P, ws_bytes=1 << 20, ptr=P)
+    a.update(kw)
+    p = a["ptr"]
+    return fa.lib().fa_bwd(P, P, P, P, P, P, p, P, P, a["B"], a["H"], a["N"], a["D"], a["causal"], a["scale"],
+                           a["dtype"], a["variant"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=9), fa.FA_ERR_INVALID_ARG),
+    (dict(variant=3), fa.FA_ERR_INVALID_ARG),
+    (dict(ws=None), fa.FA_ERR_INVALID_ARG),
+    (dict(ptr=None), fa.FA_ERR_INVALID_ARG),
+    (dict(ws_bytes=16), fa.FA_ERR_WORKSPACE),
+    (dict(D=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=-0.5), fa.FA_ERR_INVALID_ARG),
+])
+def test_bwd_validation(kw, status):
+    assert _bwd(**kw) == status
+    assert fa.last_error() != ""
+
+
+def test_error_string_is_per_thread():
+    import threading
+
+    _fwd(N=0)
+    seen = {}
+
+    def other():
+        seen["msg"] = fa.last_error()
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["msg"] == ""
+    assert fa.last_error() != ""

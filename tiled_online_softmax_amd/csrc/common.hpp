@@ -1,0 +1,118 @@
+// Shared device helpers for the gfx950 attention kernels: vector types,
+// bounds-checked buffer loads, the LDS swizzle, MFMA wrappers and the
+// wave-level reductions. CDNA4 only (wave64, MFMA, 160 KB LDS per CU).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+enum class Elt { F32, BF16, FP8 };
+
+template <Elt E> struct EltInfo;
+template <> struct EltInfo<Elt::F32> { static constexpr int bytes = 4; };
+template <> struct EltInfo<Elt::BF16> { static constexpr int bytes = 2; };
+template <> struct EltInfo<Elt::FP8> { static constexpr int bytes = 1; };
+
+// ---------------------------------------------------------------------------
+// Buffer resources: loads past `bytes` return zero instead of faulting, which
+// is how ragged tails (rows >= N) are read without branches.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ i32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+__device__ __forceinline__ float buf_load4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
+// ---------------------------------------------------------------------------
+// LDS tile layout. A tile is `rows` rows of `RB` bytes, addressed in 16-byte
+// chunks. The chunk index is XOR-swizzled with a function of the row so that
+// 16 lanes reading the same chunk column of 16 consecutive rows hit 16
+// different 16-byte bank groups (64 banks x 4 bytes = one 256-byte line).
+// ---------------------------------------------------------------------------
+template <int RB>
+__device__ __forceinline__ constexpr uint32_t lds_off(int row, int chunk) {
+  constexpr int CPR = RB / 16;  // chunks per row
+  int swz = 0;
+  if constexpr (CPR >= 16) {
+    swz = row & 15;
+  } else {
+    constexpr int RPL = 16 / CPR;  // rows per 256-byte line
+    swz = (row / RPL) & (CPR - 1);
+  }
+  return (uint32_t)(row * RB + ((chunk ^ swz) * 16));
+}
+
+// ---------------------------------------------------------------------------
+// Key permutations for operands read transposed from LDS.
+//
+// The 32x32 MFMA accumulator puts element (r, c) of a block in lane
+// c + 32*((r/4)%2), register (r/8)*4 + r%4. So a lane holding column c holds
+// rows {8a + 4h + t : a = 0..3, t = 0..3} with h = lane/32. When that
+// accumulator (probabilities over keys r) becomes the B operand of the next
+// product, lane-half h supplies keys 8a + 4h + t. The A operand, read from a
+// transposed LDS copy, must list its keys in the same order; storing key j at
+// position perm(j) makes that a contiguous 16-byte (bf16) or 32-byte (fp8)
+// read.
+// ---------------------------------------------------------------------------
+// bf16: a 16-key contraction chunk; swap bits 2 and 3 of the key.
+__device__ __forceinline__ constexpr int perm16(int j) {
+  return (j & ~15) | (((j >> 2) & 1) << 3) | (((j >> 3) & 1) << 2) | (j & 3);
+}
+// fp8: a 64-key contraction chunk made of two 32-key accumulator blocks:
+// key bits [b5 | b4 b3 | b2 | b1 b0] -> position bits [b2 | b5 | b4 b3 | b1 b0].
+__device__ __forceinline__ constexpr int perm64(int j) {
+  return (j & ~63) | (((j >> 2) & 1) << 5) | (((j >> 5) & 1) << 4) | (((j >> 3) & 3) << 2) | (j & 3);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA wrappers (gfx950).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x16 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// e4m3 x e4m3, K = 64, unit block scales (e8m0 127 = 2^0).
+__device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Exchange with the lane 32 away (the other half of a 32x32 block column).
+__device__ __forceinline__ float xor32(float x) {
+  return __shfl_xor(x, 32, 64);
+}
+
+__device__ __forceinline__ bool wave_any(bool p) {
+  return __builtin_amdgcn_ballot_w64(p) != 0;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Two floats -> two e4m3 codes (round to nearest even) in the low (HI=false)
+// or high 16 bits of `old`.
+template <bool HI>
+__device__ __forceinline__ int cvt_fp8x2(float a, float b, int old) {
+  return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
+}
+
+}  // namespace fa

@@ -1,0 +1,53 @@
+// Internal interface between the C ABI (api.cpp) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+#include "common.hpp"
+
+namespace fa {
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const float* q_descale;  // fp8 only; nullptr means 1
+  const float* k_descale;
+  const float* v_descale;
+  int N;
+  int causal;
+  int n_qtiles;        // set by the launcher
+  float scale_log2;    // scale * log2(e)
+  float rescale_log2;  // conditional-rescale threshold (base-2 units)
+};
+
+bool fwd_supported(Elt e, int D);
+hipError_t fwd_dispatch(Elt e, int D, const FwdParams& p, int B, int H, hipStream_t st);
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dO;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;     // [B,H,N] workspace: rowsum(dO * O)
+  float* dq_accum;  // [B,H,N,D] float workspace (atomic variant), else nullptr
+  int N;
+  int causal;
+  float scale;       // softmax scale
+  float scale_log2;  // scale * log2(e)
+};
+
+bool bwd_supported(int D);
+hipError_t bwd_dispatch(int D, int variant, const BwdParams& p, int B, int H, hipStream_t st);
+
+hipError_t quantize_fp8_launch(const float* x, size_t n, void* codes, float* descale, hipStream_t st);
+
+}  // namespace fa

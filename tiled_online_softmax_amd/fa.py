@@ -1,0 +1,179 @@
+"""ctypes binding for libfa.so (argument marshalling only).
+
+Every function here checks tensor placement/shape, allocates outputs with
+torch (device memory is torch's job), and calls the matching C entry point of
+include/fa.h on torch's current stream. All arithmetic runs in the HIP
+kernels; there is no fallback: if libfa.so is missing or a call fails, an
+exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_F32, FA_BF16, FA_FP8_E4M3 = 0, 1, 2
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, 1, 2, 3, 4
+FA_BWD_ATOMIC, FA_BWD_DETERMINISTIC = 0, 1
+
+EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_fwd_fp8", "fa_quantize_fp8", "fa_bwd_workspace_size", "fa_bwd",
+            "fa_status_string", "fa_last_error")
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{status_string(status)}: {message}")
+        self.status = status
+
+
+_lib = None
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfa.so (built in-tree by tiled_online_softmax_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m tiled_online_softmax_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.fa_fwd.argtypes = [_vp] * 5 + [_i] * 5 + [_f, _i, _vp]
+        L.fa_fwd_ex.argtypes = [_vp] * 5 + [_i] * 5 + [_f, _i, _f, _vp]
+        L.fa_fwd_fp8.argtypes = [_vp] * 5 + [_i] * 5 + [_f] + [_vp] * 3 + [_vp]
+        L.fa_quantize_fp8.argtypes = [_vp, _sz, _vp, _vp, _vp]
+        L.fa_bwd_workspace_size.argtypes = [_i] * 6
+        L.fa_bwd_workspace_size.restype = _sz
+        L.fa_bwd.argtypes = [_vp] * 9 + [_i] * 5 + [_f, _i, _i, _vp, _sz, _vp]
+        L.fa_status_string.argtypes = [_i]
+        L.fa_status_string.restype = ctypes.c_char_p
+        L.fa_last_error.argtypes = []
+        L.fa_last_error.restype = ctypes.c_char_p
+        for name in ("fa_fwd", "fa_fwd_ex", "fa_fwd_fp8", "fa_quantize_fp8", "fa_bwd"):
+            getattr(L, name).restype = _i
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().fa_status_string(status).decode()
+
+
+def last_error() -> str:
+    return lib().fa_last_error().decode()
+
+
+def _check(status: int):
+    if status != FA_OK:
+        raise FAError(status, last_error())
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return FA_F32
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return FA_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check_qkv(*ts: torch.Tensor):
+    ref = ts[0]
+    if ref.dim() != 4:
+        raise ValueError("tensors must be [B, H, N, D]")
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on a GPU device")
+        if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device:
+            raise ValueError("q, k, v must share shape, dtype and device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [B, H, N, D]")
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False, scale: Optional[float] = None,
+        rescale_log2: Optional[float] = None, out: Optional[torch.Tensor] = None,
+        lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Attention forward. Returns (O, lse); O is float32 for float32 inputs, bf16 otherwise."""
+    _check_qkv(q, k, v)
+    B, H, N, D = q.shape
+    code = _dtype_code(q)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32 if code == FA_F32 else torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, D, int(causal), scale,
+            code)
+    if rescale_log2 is None:
+        _check(lib().fa_fwd(*args, _stream(q)))
+    else:
+        _check(lib().fa_fwd_ex(*args, float(rescale_log2), _stream(q)))
+    return out, lse
+
+
+def fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False, scale: Optional[float] = None,
+            q_descale: Optional[torch.Tensor] = None, k_descale: Optional[torch.Tensor] = None,
+            v_descale: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+            lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """FP8 (e4m3 codes, uint8 or float8_e4m3fn tensors) forward with per-tensor descales (1-element device tensors)."""
+    _check_qkv(q, k, v)
+    B, H, N, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+
+    def ptr(t):
+        if t is None:
+            return None
+        if t.dtype != torch.float32 or not t.is_cuda or t.numel() < 1:
+            raise ValueError("descales must be float32 device tensors with one element")
+        return t.data_ptr()
+
+    _check(lib().fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, D,
+                            int(causal), scale, ptr(q_descale), ptr(k_descale), ptr(v_descale), _stream(q)))
+    return out, lse
+
+
+def quantize_fp8(x: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per-tensor e4m3 quantisation of a float32 device tensor: returns (codes uint8, descale float32[1])."""
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("quantize_fp8 takes a contiguous float32 device tensor")
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    descale = torch.empty(1, dtype=torch.float32, device=x.device)
+    _check(lib().fa_quantize_fp8(x.data_ptr(), x.numel(), codes.data_ptr(), descale.data_ptr(), _stream(x)))
+    return codes, descale
+
+
+def bwd_workspace_size(B: int, H: int, N: int, D: int, variant: int = FA_BWD_ATOMIC) -> int:
+    return int(lib().fa_bwd_workspace_size(B, H, N, D, FA_BF16, variant))
+
+
+def bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None, variant: int = FA_BWD_ATOMIC,
+        workspace: Optional[torch.Tensor] = None, dq=None, dk=None, dv=None):
+    """Attention backward (bf16). Returns (dQ, dK, dV) as bf16 tensors."""
+    _check_qkv(q, k, v, o, do)
+    B, H, N, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if lse.dtype != torch.float32 or lse.shape != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, N]")
+    need = bwd_workspace_size(B, H, N, D, variant)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check(lib().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, D, int(causal), scale, _dtype_code(q),
+                        variant, workspace.data_ptr(), workspace.numel(), _stream(q)))
+    return dq, dk, dv
