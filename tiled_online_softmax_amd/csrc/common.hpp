@@ -62,6 +62,75 @@ __device__ __forceinline__ constexpr uint32_t lds_off(int row, int chunk) {
 }
 
 // ---------------------------------------------------------------------------
+// Row-major LDS tiles written by direct global->LDS loads.
+//
+// A tile holds rows of RB bytes, viewed as 256-byte lines (64 banks x 4 B)
+// and 16-byte chunks. The chunk position inside a line is XOR-swizzled with
+// a bijection of the row so that
+//   * 16 lanes reading the same chunk of 16 consecutive rows (an MFMA operand
+//     read with ds_read_b128) hit 16 different bank groups, and
+//   * a ds_read_b64_tr_b16 over 4 consecutive rows x 64 bytes by 32 lanes
+//     covers 64 different banks (rows differing in the two low bits land in
+//     different 64-byte groups of the line).
+// tile_off(row, chunk) is the byte offset of logical chunk `chunk` of `row`;
+// tile_pos(phys16) inverts it for the loader, which writes lane-linear 16-byte
+// positions.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ constexpr int swz16(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ constexpr int swz8(int x) { return ((x & 1) << 2) | ((x >> 1) & 3); }
+
+template <int RB>
+__device__ __forceinline__ constexpr uint32_t tile_off(int row, int chunk) {
+  static_assert(RB == 128 || RB % 256 == 0, "row size");
+  if constexpr (RB >= 256) {
+    constexpr int LPR = RB / 256;  // lines per row
+    return (uint32_t)((row * LPR + (chunk >> 4)) * 256 + (((chunk & 15) ^ swz16(row & 15)) << 4));
+  } else {
+    return (uint32_t)((row >> 1) * 256 + (((row & 1) << 3) + ((chunk & 7) ^ swz8((row >> 1) & 7))) * 16);
+  }
+}
+
+// Inverse of tile_off: physical 16-byte slot -> (row, logical chunk).
+template <int RB>
+__device__ __forceinline__ void tile_pos(int phys, int& row, int& chunk) {
+  const int line = phys >> 4, pos = phys & 15;
+  if constexpr (RB >= 256) {
+    constexpr int LPR = RB / 256;
+    row = line / LPR;
+    chunk = (line % LPR) * 16 + (pos ^ swz16(row & 15));
+  } else {
+    row = 2 * line + (pos >> 3);
+    chunk = (pos & 7) ^ swz8(line & 7);
+  }
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// 16 bytes per lane from a buffer straight into LDS at lds_base + 16 * lane.
+__device__ __forceinline__ void buf_load_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                               lds_void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 16, (int)voff, (int)soff, 0, 0);
+}
+
+// Transposing 8-byte LDS read of 16-bit elements (gfx950). Within each group
+// of 16 lanes, lane j supplies the address of 4 consecutive elements M[j][0..3];
+// lane j' receives M[4i + j'/4][j' % 4] for i = 0..3.
+__device__ __forceinline__ s16x4 lds_read_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
+
+// vmcnt(0): all of this wave's vector-memory operations (incl. LDS DMA) done.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+__device__ __forceinline__ float dot2_bf16_sum(int packed_pair, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed_pair), one, acc, false);
+}
+
+// ---------------------------------------------------------------------------
 // Key permutations for operands read transposed from LDS.
 //
 // The 32x32 MFMA accumulator puts element (r, c) of a block in lane
