@@ -121,7 +121,7 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int D, int dtype, int variant)
   if (B < 1 || H < 1 || N < 1 || D < 1 || dtype != FA_BF16) return 0;
   if (variant != FA_BWD_ATOMIC && variant != FA_BWD_DETERMINISTIC) return 0;
   const size_t rows = (size_t)B * H * N;
-  size_t bytes = (rows * sizeof(float) + 255) & ~(size_t)255;
+  size_t bytes = (rows * 2 * sizeof(float) + 255) & ~(size_t)255;
   if (variant == FA_BWD_ATOMIC) bytes += rows * (size_t)D * sizeof(float);
   return bytes;
 }
@@ -143,10 +143,10 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   fa::BwdParams p{};
   p.q = q; p.k = k; p.v = v; p.o = o; p.dO = dO; p.lse = lse;
   p.dq = dq; p.dk = dk; p.dv = dv;
-  p.delta = reinterpret_cast<float*>(workspace);
+  p.ld = reinterpret_cast<float*>(workspace);
   const size_t rows = (size_t)B * H * N;
   p.dq_accum = variant == FA_BWD_ATOMIC
-                   ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + ((rows * sizeof(float) + 255) & ~(size_t)255))
+                   ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + ((rows * 2 * sizeof(float) + 255) & ~(size_t)255))
                    : nullptr;
   p.N = N; p.causal = causal; p.scale = scale; p.scale_log2 = scale * fa::kLog2e;
   return hip_status(fa::bwd_dispatch(D, variant, p, B, H, reinterpret_cast<hipStream_t>(stream)), "fa_bwd launch");

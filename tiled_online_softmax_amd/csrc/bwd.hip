@@ -16,10 +16,11 @@
 // CDNA4 mapping. The key-tile kernel computes S = Q K^T with 32x32 MFMAs so a
 // lane holds one key's scores for 16 queries: dV^T += dO^T P and
 // dK^T += Q^T dS then take P and dS straight from registers, with K^T and V^T
-// held in registers for the whole pass and Q, dO (row-major and transposed)
-// streamed through double-buffered LDS. The query-tile dQ kernel mirrors the
+// held in registers for the whole pass. Q and dO tiles are copied row-major
+// into LDS by LDS-DMA loads and read both directly (S, dP) and transposed
+// (ds_read_b64_tr_b16 for Q^T, dO^T). The query-tile dQ kernel mirrors the
 // forward: S^T = K Q^T and dP^T = V dO^T put one query per lane, so lse and D
-// are per-lane scalars, and dQ^T += K^T dS^T reads a transposed K tile.
+// are per-lane scalars, and dQ^T += K^T dS^T reads K^T with transposing reads.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -28,13 +29,13 @@ namespace fa {
 constexpr float kInf = __builtin_huge_valf();
 
 // ---------------------------------------------------------------------------
-// D_i = sum_d dO_id O_id (float32); the atomic variant also zeroes dQ_accum.
-// One thread per 8 consecutive elements of a row.
+// ld[row] = (lse * log2(e), D = sum_d dO O) as a float pair; the atomic variant
+// also zeroes dQ_accum. One thread per 8 consecutive elements of a row.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ dO,
-                                                      float* __restrict__ delta, float* __restrict__ dq_accum,
-                                                      long long rows) {
+                                                      const float* __restrict__ lse, float* __restrict__ ld,
+                                                      float* __restrict__ dq_accum, long long rows) {
   constexpr int TPR = D / 8;  // threads per row
   const long long gt = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long row = gt / TPR;
@@ -53,7 +54,10 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const __bf16* __restrict__
   }
 #pragma unroll
   for (int o2 = TPR / 2; o2 > 0; o2 >>= 1) s += __shfl_xor(s, o2, 64);
-  if (row < rows && part == 0) delta[row] = s;
+  if (row < rows && part == 0) {
+    ld[2 * row] = lse[row] * kLog2e;
+    ld[2 * row + 1] = s;
+  }
 }
 
 // dQ = bf16(dQ_accum) (the scale is already applied).
@@ -72,82 +76,39 @@ __global__ void __launch_bounds__(256) bwd_dq_convert_kernel(const float* __rest
   *reinterpret_cast<bf16x8*>(dq + 8 * i) = r;
 }
 
-// Writes the 8 bf16 of a 16-byte global chunk (row `row`, columns 8ch..8ch+7)
-// into a transposed LDS tile T[col][perm16(row)] of RB bytes per column row.
-template <int RB>
-__device__ __forceinline__ void store_transposed_bf16(char* base, int row, int ch, const i32x4& data) {
-  const int p = perm16(row);
-  const unsigned short* e = reinterpret_cast<const unsigned short*>(&data);
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    *reinterpret_cast<unsigned short*>(base + lds_off<RB>(8 * ch + i, p >> 3) + (p & 7) * 2) = e[i];
-}
+template <int S> struct BStage { static constexpr int value = S; };
 
 // ---------------------------------------------------------------------------
-// Key-tile pass: dK, dV (and atomic dQ).
+// Key-tile pass: dK, dV (and, for the atomic variant, dQ by float atomics).
 // ---------------------------------------------------------------------------
 template <int D_, int NW_, int BQ_, int OCC_>
 struct DkdvCfg {
   static constexpr int D = D_, NW = NW_, BQ = BQ_, OCC = OCC_;
   static constexpr int BK = 32 * NW;    // keys per workgroup (32 per wave)
   static constexpr int NT = 64 * NW;
-  static constexpr int RB = D * 2;      // bytes per row-major Q / dO row
-  static constexpr int RBT = BQ * 2;    // bytes per transposed row (BQ queries)
-  static constexpr int Q_BYTES = BQ * RB;
-  static constexpr int QT_BYTES = D * RBT;
-  static constexpr int OFF_QT = Q_BYTES;
-  static constexpr int OFF_DO = OFF_QT + QT_BYTES;
-  static constexpr int OFF_DOT = OFF_DO + Q_BYTES;
-  static constexpr int OFF_LSE = OFF_DOT + QT_BYTES;
-  static constexpr int OFF_DELTA = OFF_LSE + BQ * 4;
-  static constexpr int STAGE = OFF_DELTA + BQ * 4;
-  static constexpr int RB_KT = BK * 2;  // transposed K rows (atomic variant)
-  static constexpr int KT_BYTES = D * RB_KT;
-  static constexpr int RB_DS = BK * 2;  // dS tile [BQ queries][BK keys]
-  static constexpr int DS_BYTES = BQ * RB_DS;
-  static constexpr int CPR = RB / 16;
-  static constexpr int CPT = BQ * CPR / NT;  // 16-byte chunks per thread per Q (and dO) tile
-  static constexpr int NP = RB / 32;         // K^T / V^T register pieces per lane
-  static_assert((BQ * CPR) % NT == 0 && BQ % 32 == 0 && D % 32 == 0, "tile shape");
+  static constexpr int RB = D * 2;      // bytes per Q / dO / K row
+  static constexpr int QTILE = BQ * RB; // one Q (or dO) tile
+  static constexpr int OFF_DO = QTILE;
+  static constexpr int OFF_LD = 2 * QTILE;
+  static constexpr int STAGE = 2 * QTILE + 1024;  // + (lse*log2e, D) pairs, BQ*8 <= 1 KB
+  static constexpr int KTILE = BK * RB;           // K tile (atomic variant)
+  static constexpr int RB_DS = BQ * 2;            // dS^T tile: [key][query] bf16
+  static constexpr int DSTILE = BK * RB_DS;
+  static constexpr int LPW = QTILE / 1024 / NW;   // DMA loads per wave per Q (dO) tile
+  static constexpr int KLPW = KTILE / 1024 / NW;
+  static constexpr int NP = RB / 32;
+  static constexpr int NA = BQ / 32, NE = D / 32;
+  static_assert(QTILE % (1024 * NW) == 0 && BQ * 8 <= 1024 && BQ % 32 == 0, "tile shape");
+  static_assert(RB_DS == 128 || RB_DS % 256 == 0, "dS tile row");
 };
-
-template <class C>
-__device__ __forceinline__ void dkdv_load(const __amdgpu_buffer_rsrc_t& rq, const __amdgpu_buffer_rsrc_t& rdo,
-                                          int q0, int tid, i32x4* qr, i32x4* dor) {
-#pragma unroll
-  for (int r = 0; r < C::CPT; ++r) {
-    const int c = tid + C::NT * r;
-    const uint32_t off = (uint32_t)(q0 + c / C::CPR) * C::RB + (c % C::CPR) * 16;
-    qr[r] = buf_load16(rq, off);
-    dor[r] = buf_load16(rdo, off);
-  }
-}
-
-template <class C>
-__device__ __forceinline__ void dkdv_store(char* st, int tid, const i32x4* qr, const i32x4* dor, float lse_l2,
-                                           float dlt) {
-#pragma unroll
-  for (int r = 0; r < C::CPT; ++r) {
-    const int c = tid + C::NT * r;
-    const int row = c / C::CPR, ch = c % C::CPR;
-    *reinterpret_cast<i32x4*>(st + lds_off<C::RB>(row, ch)) = qr[r];
-    *reinterpret_cast<i32x4*>(st + C::OFF_DO + lds_off<C::RB>(row, ch)) = dor[r];
-    store_transposed_bf16<C::RBT>(st + C::OFF_QT, row, ch, qr[r]);
-    store_transposed_bf16<C::RBT>(st + C::OFF_DOT, row, ch, dor[r]);
-  }
-  if (tid < C::BQ) {
-    reinterpret_cast<float*>(st + C::OFF_LSE)[tid] = lse_l2;
-    reinterpret_cast<float*>(st + C::OFF_DELTA)[tid] = dlt;
-  }
-}
 
 template <class C, bool ATOMIC>
 __global__ void __launch_bounds__(C::NT)
 __attribute__((amdgpu_waves_per_eu(C::OCC, C::OCC)))
 bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
-  constexpr int D = C::D, BQ = C::BQ, NE = D / 32, NA = BQ / 32;
-  constexpr int SMEM = 2 * C::STAGE + (ATOMIC ? C::KT_BYTES + C::DS_BYTES : 0);
-  __shared__ __attribute__((aligned(16))) char smem[SMEM];
+  constexpr int D = C::D, BQ = C::BQ, NE = C::NE, NA = C::NA, RB = C::RB, NP = C::NP;
+  constexpr int SMEM = 2 * C::STAGE + (ATOMIC ? C::KTILE + C::DSTILE : 0);
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 31, hf = lane >> 5;
 
   const int G = gridDim.x;
@@ -166,27 +127,56 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
   const auto rk = make_rsrc(reinterpret_cast<const __bf16*>(P.k) + head, head_bytes);
   const auto rv = make_rsrc(reinterpret_cast<const __bf16*>(P.v) + head, head_bytes);
   const auto rdo = make_rsrc(reinterpret_cast<const __bf16*>(P.dO) + head, head_bytes);
-  const float* lse_h = P.lse + (size_t)bh * N;
-  const float* dl_h = P.delta + (size_t)bh * N;
+  const auto rld = make_rsrc(P.ld + (size_t)bh * N * 2, (uint32_t)((size_t)N * 8));
 
   // K^T and V^T pieces (B operands of S = Q K^T and dP = dO V^T).
-  i32x4 kf[C::NP], vf[C::NP];
+  i32x4 kf[NP], vf[NP];
 #pragma unroll
-  for (int p = 0; p < C::NP; ++p) {
-    kf[p] = buf_load16(rk, (uint32_t)key * C::RB + 32 * p + 16 * hf);
-    vf[p] = buf_load16(rv, (uint32_t)key * C::RB + 32 * p + 16 * hf);
+  for (int p = 0; p < NP; ++p) {
+    kf[p] = buf_load16(rk, (uint32_t)key * RB + 32 * p + 16 * hf);
+    vf[p] = buf_load16(rv, (uint32_t)key * RB + 32 * p + 16 * hf);
   }
+
+  uint32_t goff[C::LPW];
+#pragma unroll
+  for (int i = 0; i < C::LPW; ++i) {
+    int row, ch;
+    tile_pos<RB>((wave * C::LPW + i) * 64 + lane, row, ch);
+    goff[i] = (uint32_t)(row * RB + ch * 16);
+  }
+  auto issue = [&](int q0, int stage) {
+    char* st = smem + stage * C::STAGE;
+    const uint32_t base = (uint32_t)q0 * RB;
+#pragma unroll
+    for (int i = 0; i < C::LPW; ++i) {
+      const int m = wave * C::LPW + i;
+      buf_load_lds16(rq, goff[i] + base, 0, (lds_void*)(st + m * 1024));
+      buf_load_lds16(rdo, goff[i] + base, 0, (lds_void*)(st + C::OFF_DO + m * 1024));
+    }
+    if (wave == 0 && lane < BQ / 2) buf_load_lds16(rld, (uint32_t)(q0 * 8 + lane * 16), 0, (lds_void*)(st + C::OFF_LD));
+  };
+
   char* kt_lds = smem + 2 * C::STAGE;
-  char* ds_lds = kt_lds + C::KT_BYTES;
+  char* ds_lds = kt_lds + C::KTILE;
   if constexpr (ATOMIC) {
-    // K tile transposed: KT[d][perm16(key - k0)]
-    constexpr int CH = C::BK * C::CPR;
-    for (int c = tid; c < CH; c += C::NT) {
-      const int row = c / C::CPR, ch = c % C::CPR;
-      const i32x4 x = buf_load16(rk, (uint32_t)(k0 + row) * C::RB + ch * 16);
-      store_transposed_bf16<C::RB_KT>(kt_lds, row, ch, x);
+#pragma unroll
+    for (int i = 0; i < C::KLPW; ++i) {
+      const int m = wave * C::KLPW + i;
+      int row, ch;
+      tile_pos<RB>(m * 64 + lane, row, ch);
+      buf_load_lds16(rk, (uint32_t)((k0 + row) * RB + ch * 16), 0, (lds_void*)(kt_lds + m * 1024));
     }
   }
+
+  // Per-lane LDS offsets.
+  uint32_t qoff[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) qoff[p] = tile_off<RB>(li, 2 * p + hf);
+  uint32_t troff[NE][2];  // Q^T / dO^T operands, query order of the S accumulator
+#pragma unroll
+  for (int e = 0; e < NE; ++e)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) troff[e][u] = tr16_off<RB, true>(lane, e, u);
 
   f32x16 adk[NE], adv[NE];
 #pragma unroll
@@ -199,27 +189,18 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
   const int nq = (N + BQ - 1) / BQ;
   const float sl2 = P.scale_log2;
 
-  i32x4 qr[C::CPT], dor[C::CPT];
-  float lse_n = 0.f, dl_n = 0.f;
-  auto fetch_rows = [&](int q0) {
-    dkdv_load<C>(rq, rdo, q0, tid, qr, dor);
-    if (tid < BQ) {
-      const int q = q0 + tid;
-      lse_n = q < N ? lse_h[q] * kLog2e : kInf;
-      dl_n = q < N ? dl_h[q] : 0.f;
-    }
-  };
-  fetch_rows(qt0 * BQ);
-  dkdv_store<C>(smem, tid, qr, dor, lse_n, dl_n);
+  issue(qt0 * BQ, 0);
+  wait_vmem();
   __syncthreads();
 
-  for (int it = qt0; it < nq; ++it) {
+  auto tile = [&](int it, auto stage_tag) {
+    constexpr int S = decltype(stage_tag)::value;
     const int q0 = it * BQ;
     const bool more = it + 1 < nq;
-    if (more) fetch_rows(q0 + BQ);
-    const char* st = smem + ((it - qt0) & 1) * C::STAGE;
-    const float* lse_s = reinterpret_cast<const float*>(st + C::OFF_LSE);
-    const float* dl_s = reinterpret_cast<const float*>(st + C::OFF_DELTA);
+    if (more) issue(q0 + BQ, S ^ 1);
+    const char* qs = smem + S * C::STAGE;
+    const char* dos = qs + C::OFF_DO;
+    const float* lds_ld = reinterpret_cast<const float*>(qs + C::OFF_LD);
 
     const bool live = !P.causal || q0 + BQ - 1 >= kw;
     f32x16 s[NA], dp[NA];
@@ -229,29 +210,34 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
         s[a] = f32x16{};
         dp[a] = f32x16{};
 #pragma unroll
-        for (int p = 0; p < C::NP; ++p) {
-          const i32x4 x = *reinterpret_cast<const i32x4*>(st + lds_off<C::RB>(32 * a + li, 2 * p + hf));
+        for (int p = 0; p < NP; ++p) {
+          const i32x4 x = *reinterpret_cast<const i32x4*>(qs + qoff[p] + 32 * a * RB);
           s[a] = mfma_bf16(__builtin_bit_cast(bf16x8, x), __builtin_bit_cast(bf16x8, kf[p]), s[a]);
-          const i32x4 y = *reinterpret_cast<const i32x4*>(st + C::OFF_DO + lds_off<C::RB>(32 * a + li, 2 * p + hf));
+          const i32x4 y = *reinterpret_cast<const i32x4*>(dos + qoff[p] + 32 * a * RB);
           dp[a] = mfma_bf16(__builtin_bit_cast(bf16x8, y), __builtin_bit_cast(bf16x8, vf[p]), dp[a]);
         }
       }
-      // P = 2^(s*sl2 - lse*log2e) and dS = P (dP - D); rows are queries 32a + 8g + 4h + t.
-      const bool mask = P.causal && q0 < kw + 31;
+      // P = 2^(s*sl2 - lse*log2e), dS = P (dP - D); accumulator rows are queries 32a + 8g + 4h + t.
+      const bool mask = (P.causal && q0 < kw + 31) || (q0 + BQ > N);
 #pragma unroll
       for (int a = 0; a < NA; ++a)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int qb = 32 * a + 8 * g + 4 * hf;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_s + qb);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dl_s + qb);
+          const f32x4 x0 = *reinterpret_cast<const f32x4*>(lds_ld + 2 * qb);      // (l2,d) rows qb, qb+1
+          const f32x4 x1 = *reinterpret_cast<const f32x4*>(lds_ld + 2 * qb + 4);  // rows qb+2, qb+3
+          const float l2[4] = {x0[0], x0[2], x1[0], x1[2]};
+          const float dd[4] = {x0[1], x0[3], x1[1], x1[3]};
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const int v = 4 * g + t;
-            float pv = fast_exp2(__builtin_fmaf(s[a][v], sl2, -l4[t]));
-            if (mask && key > q0 + qb + t) pv = 0.f;
+            float pv = fast_exp2(__builtin_fmaf(s[a][v], sl2, -l2[t]));
+            if (mask) {
+              const int q = q0 + qb + t;
+              if (q >= N || (P.causal && key > q)) pv = 0.f;
+            }
             s[a][v] = pv;
-            dp[a][v] = pv * (dp[a][v] - d4[t]);
+            dp[a][v] = pv * (dp[a][v] - dd[t]);
           }
         }
       // dV^T += dO^T P ; dK^T += Q^T dS (contraction over 16-query chunks)
@@ -265,35 +251,39 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
         }
 #pragma unroll
         for (int e = 0; e < NE; ++e) {
-          const i32x4 x = *reinterpret_cast<const i32x4*>(st + C::OFF_DOT + lds_off<C::RBT>(32 * e + li, 2 * kc + hf));
+          const s16x4 x[2] = {lds_read_tr16(dos + troff[e][0] + kc * 16 * RB),
+                              lds_read_tr16(dos + troff[e][1] + kc * 16 * RB)};
           adv[e] = mfma_bf16(__builtin_bit_cast(bf16x8, x), pb, adv[e]);
-          const i32x4 y = *reinterpret_cast<const i32x4*>(st + C::OFF_QT + lds_off<C::RBT>(32 * e + li, 2 * kc + hf));
+          const s16x4 y[2] = {lds_read_tr16(qs + troff[e][0] + kc * 16 * RB),
+                              lds_read_tr16(qs + troff[e][1] + kc * 16 * RB)};
           adk[e] = mfma_bf16(__builtin_bit_cast(bf16x8, y), db, adk[e]);
         }
       }
     }
 
     if constexpr (ATOMIC) {
-      // dS (bf16) -> LDS as [query][perm16(key)], then dQ_tile += dS K over this
-      // workgroup's BK keys, added into the float32 scratch with atomics.
-      const int kp = perm16(32 * wave + li);
+      // dS^T (bf16) -> LDS [key][query]; each lane writes its 16 queries as 4 x 8 bytes.
+      const int kr = 32 * wave + li;
 #pragma unroll
       for (int a = 0; a < NA; ++a)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int qr_ = 32 * a + (v >> 2) * 8 + 4 * hf + (v & 3);
-          const __bf16 x = live ? (__bf16)dp[a][v] : (__bf16)0.f;
-          *reinterpret_cast<__bf16*>(ds_lds + lds_off<C::RB_DS>(qr_, kp >> 3) + (kp & 7) * 2) = x;
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 x4;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) x4[t] = live ? (__bf16)dp[a][4 * g + t] : (__bf16)0.f;
+          *reinterpret_cast<bf16x4*>(ds_lds + tile_off<C::RB_DS>(kr, 4 * a + g) + 8 * hf) = x4;
         }
       __syncthreads();
-      constexpr int NBLK = NA * NE;  // 32x32 blocks of the BQ x D dQ tile
-      for (int blk = wave; blk < NBLK; blk += C::NW) {
+      // dQ tile (BQ x D) += dS K over this workgroup's BK keys; one 32x32 block per wave per step.
+      for (int blk = wave; blk < NA * NE; blk += C::NW) {
         const int a = blk / NE, e = blk % NE;
         f32x16 c = f32x16{};
 #pragma unroll
         for (int kc = 0; kc < C::BK / 16; ++kc) {
-          const i32x4 x = *reinterpret_cast<const i32x4*>(ds_lds + lds_off<C::RB_DS>(32 * a + li, 2 * kc + hf));
-          const i32x4 y = *reinterpret_cast<const i32x4*>(kt_lds + lds_off<C::RB_KT>(32 * e + li, 2 * kc + hf));
+          const s16x4 x[2] = {lds_read_tr16(ds_lds + tr16_off<C::RB_DS, false>(lane, a, 0) + kc * 16 * C::RB_DS),
+                              lds_read_tr16(ds_lds + tr16_off<C::RB_DS, false>(lane, a, 1) + kc * 16 * C::RB_DS)};
+          const s16x4 y[2] = {lds_read_tr16(kt_lds + tr16_off<RB, false>(lane, e, 0) + kc * 16 * RB),
+                              lds_read_tr16(kt_lds + tr16_off<RB, false>(lane, e, 1) + kc * 16 * RB)};
           c = mfma_bf16(__builtin_bit_cast(bf16x8, x), __builtin_bit_cast(bf16x8, y), c);
         }
         float* dst = P.dq_accum + ((size_t)bh * N) * D + 32 * e + li;
@@ -305,11 +295,12 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
       }
     }
 
-    if (more) {
-      float l = lse_n, d = dl_n;
-      dkdv_store<C>(smem + ((it - qt0 + 1) & 1) * C::STAGE, tid, qr, dor, l, d);
-    }
+    if (more) wait_vmem();
     __syncthreads();
+  };
+  for (int it = qt0; it < nq; it += 2) {
+    tile(it, BStage<0>{});
+    if (it + 1 < nq) tile(it + 1, BStage<1>{});
   }
 
   if (key < N) {
@@ -341,23 +332,20 @@ struct DqCfg {
   static constexpr int BM = 32 * NW;
   static constexpr int NT = 64 * NW;
   static constexpr int RB = D * 2;
-  static constexpr int RBT = BN * 2;
-  static constexpr int K_BYTES = BN * RB;
-  static constexpr int OFF_V = K_BYTES;
-  static constexpr int OFF_KT = 2 * K_BYTES;
-  static constexpr int STAGE = OFF_KT + D * RBT;
-  static constexpr int CPR = RB / 16;
-  static constexpr int CPT = BN * CPR / NT;
+  static constexpr int TILE = BN * RB;
+  static constexpr int STAGE = 2 * TILE;  // K tile, then V tile
+  static constexpr int LPW = TILE / 1024 / NW;
   static constexpr int NP = RB / 32;
-  static_assert((BN * CPR) % NT == 0 && BN % 32 == 0, "tile shape");
+  static constexpr int NB = BN / 32, NE = D / 32;
+  static_assert(TILE % (1024 * NW) == 0 && BN % 32 == 0, "tile shape");
 };
 
 template <class C>
 __global__ void __launch_bounds__(C::NT)
 __attribute__((amdgpu_waves_per_eu(C::OCC, C::OCC)))
 bwd_dq_kernel(BwdParams P, int n_qtiles) {
-  constexpr int D = C::D, BN = C::BN, NB = BN / 32, NE = D / 32;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
+  constexpr int D = C::D, BN = C::BN, NB = C::NB, NE = C::NE, RB = C::RB, NP = C::NP;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 31, hf = lane >> 5;
 
   const int G = gridDim.x;
@@ -378,15 +366,44 @@ bwd_dq_kernel(BwdParams P, int n_qtiles) {
   const auto rv = make_rsrc(reinterpret_cast<const __bf16*>(P.v) + head, head_bytes);
   const auto rdo = make_rsrc(reinterpret_cast<const __bf16*>(P.dO) + head, head_bytes);
 
-  i32x4 qf[C::NP], dof[C::NP];
+  i32x4 qf[NP], dof[NP];
 #pragma unroll
-  for (int p = 0; p < C::NP; ++p) {
-    qf[p] = buf_load16(rq, (uint32_t)qrow * C::RB + 32 * p + 16 * hf);
-    dof[p] = buf_load16(rdo, (uint32_t)qrow * C::RB + 32 * p + 16 * hf);
+  for (int p = 0; p < NP; ++p) {
+    qf[p] = buf_load16(rq, (uint32_t)qrow * RB + 32 * p + 16 * hf);
+    dof[p] = buf_load16(rdo, (uint32_t)qrow * RB + 32 * p + 16 * hf);
   }
-  const float lse_l2 = qrow < N ? P.lse[(size_t)bh * N + qrow] * kLog2e : kInf;
-  const float dlt = qrow < N ? P.delta[(size_t)bh * N + qrow] : 0.f;
+  float lse_l2 = kInf, dlt = 0.f;
+  if (qrow < N) {
+    lse_l2 = P.ld[2 * ((size_t)bh * N + qrow)];
+    dlt = P.ld[2 * ((size_t)bh * N + qrow) + 1];
+  }
   const float sl2 = P.scale_log2;
+
+  uint32_t goff[C::LPW];
+#pragma unroll
+  for (int i = 0; i < C::LPW; ++i) {
+    int row, ch;
+    tile_pos<RB>((wave * C::LPW + i) * 64 + lane, row, ch);
+    goff[i] = (uint32_t)(row * RB + ch * 16);
+  }
+  auto issue = [&](int key0, int stage) {
+    char* kb = smem + stage * C::STAGE;
+    const uint32_t base = (uint32_t)key0 * RB;
+#pragma unroll
+    for (int i = 0; i < C::LPW; ++i) {
+      const int m = wave * C::LPW + i;
+      buf_load_lds16(rk, goff[i] + base, 0, (lds_void*)(kb + m * 1024));
+      buf_load_lds16(rv, goff[i] + base, 0, (lds_void*)(kb + C::TILE + m * 1024));
+    }
+  };
+  uint32_t koff[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) koff[p] = tile_off<RB>(li, 2 * p + hf);
+  uint32_t troff[NE][2];  // K^T operands, key order of the S^T accumulator
+#pragma unroll
+  for (int e = 0; e < NE; ++e)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) troff[e][u] = tr16_off<RB, true>(lane, e, u);
 
   f32x16 acc[NE];
 #pragma unroll
@@ -395,35 +412,17 @@ bwd_dq_kernel(BwdParams P, int n_qtiles) {
   const int kv_end = P.causal ? min(N, q0 + C::BM) : N;
   const int n_tiles = (kv_end + BN - 1) / BN;
 
-  i32x4 kr[C::CPT], vr[C::CPT];
-  auto load = [&](int key0) {
-#pragma unroll
-    for (int r = 0; r < C::CPT; ++r) {
-      const int c = tid + C::NT * r;
-      const uint32_t off = (uint32_t)(key0 + c / C::CPR) * C::RB + (c % C::CPR) * 16;
-      kr[r] = buf_load16(rk, off);
-      vr[r] = buf_load16(rv, off);
-    }
-  };
-  auto store = [&](char* st) {
-#pragma unroll
-    for (int r = 0; r < C::CPT; ++r) {
-      const int c = tid + C::NT * r;
-      const int row = c / C::CPR, ch = c % C::CPR;
-      *reinterpret_cast<i32x4*>(st + lds_off<C::RB>(row, ch)) = kr[r];
-      *reinterpret_cast<i32x4*>(st + C::OFF_V + lds_off<C::RB>(row, ch)) = vr[r];
-      store_transposed_bf16<C::RBT>(st + C::OFF_KT, row, ch, kr[r]);
-    }
-  };
-  load(0);
-  store(smem);
+  issue(0, 0);
+  wait_vmem();
   __syncthreads();
 
-  for (int t = 0; t < n_tiles; ++t) {
+  auto tile = [&](int t, auto stage_tag) {
+    constexpr int S = decltype(stage_tag)::value;
     const int key0 = t * BN;
     const bool more = t + 1 < n_tiles;
-    if (more) load(key0 + BN);
-    const char* st = smem + (t & 1) * C::STAGE;
+    if (more) issue(key0 + BN, S ^ 1);
+    const char* ks = smem + S * C::STAGE;
+    const char* vs = ks + C::TILE;
     if (!P.causal || key0 <= qw + 31) {
       f32x16 s[NB], dp[NB];
 #pragma unroll
@@ -431,10 +430,10 @@ bwd_dq_kernel(BwdParams P, int n_qtiles) {
         s[b] = f32x16{};
         dp[b] = f32x16{};
 #pragma unroll
-        for (int p = 0; p < C::NP; ++p) {
-          const i32x4 x = *reinterpret_cast<const i32x4*>(st + lds_off<C::RB>(32 * b + li, 2 * p + hf));
+        for (int p = 0; p < NP; ++p) {
+          const i32x4 x = *reinterpret_cast<const i32x4*>(ks + koff[p] + 32 * b * RB);
           s[b] = mfma_bf16(__builtin_bit_cast(bf16x8, x), __builtin_bit_cast(bf16x8, qf[p]), s[b]);
-          const i32x4 y = *reinterpret_cast<const i32x4*>(st + C::OFF_V + lds_off<C::RB>(32 * b + li, 2 * p + hf));
+          const i32x4 y = *reinterpret_cast<const i32x4*>(vs + koff[p] + 32 * b * RB);
           dp[b] = mfma_bf16(__builtin_bit_cast(bf16x8, y), __builtin_bit_cast(bf16x8, dof[p]), dp[b]);
         }
       }
@@ -457,13 +456,18 @@ bwd_dq_kernel(BwdParams P, int n_qtiles) {
         for (int i = 0; i < 8; ++i) db[i] = (__bf16)dp[kc >> 1][(kc & 1) * 8 + i];
 #pragma unroll
         for (int e = 0; e < NE; ++e) {
-          const i32x4 x = *reinterpret_cast<const i32x4*>(st + C::OFF_KT + lds_off<C::RBT>(32 * e + li, 2 * kc + hf));
+          const s16x4 x[2] = {lds_read_tr16(ks + troff[e][0] + kc * 16 * RB),
+                              lds_read_tr16(ks + troff[e][1] + kc * 16 * RB)};
           acc[e] = mfma_bf16(__builtin_bit_cast(bf16x8, x), db, acc[e]);
         }
       }
     }
-    if (more) store(smem + ((t + 1) & 1) * C::STAGE);
+    if (more) wait_vmem();
     __syncthreads();
+  };
+  for (int t = 0; t < n_tiles; t += 2) {
+    tile(t, BStage<0>{});
+    if (t + 1 < n_tiles) tile(t + 1, BStage<1>{});
   }
 
   if (qrow < N) {
@@ -484,8 +488,8 @@ template <int D>
 static hipError_t launch_pre(const BwdParams& p, long long rows, hipStream_t st) {
   const long long threads = rows * (D / 8);
   hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
-                     reinterpret_cast<const __bf16*>(p.o), reinterpret_cast<const __bf16*>(p.dO), p.delta, p.dq_accum,
-                     rows);
+                     reinterpret_cast<const __bf16*>(p.o), reinterpret_cast<const __bf16*>(p.dO), p.lse, p.ld,
+                     p.dq_accum, rows);
   return hipGetLastError();
 }
 
@@ -509,17 +513,18 @@ static hipError_t launch_bwd(int variant, const BwdParams& p, int B, int H, hipS
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int nq = (p.N + QC::BM - 1) / QC::BM;
   const long long gq = (long long)nq * B * H;
+  if (gq > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(bwd_dq_kernel<QC>, dim3((unsigned)gq), dim3(QC::NT), 0, st, p, nq);
   return hipGetLastError();
 }
 
 bool bwd_supported(int D) { return D == 64 || D == 128; }
 
-// Parameter table for the backward: D -> (waves, query tile of the key pass,
-// key tile of the dQ pass, waves per SIMD).
+// Parameter table for the backward: D -> key pass (waves, query tile, waves
+// per SIMD) and dQ pass (waves, key tile, waves per SIMD).
 hipError_t bwd_dispatch(int D, int variant, const BwdParams& p, int B, int H, hipStream_t st) {
-  if (D == 64) return launch_bwd<DkdvCfg<64, 4, 64, 1>, DqCfg<64, 4, 64, 2>>(variant, p, B, H, st);
-  if (D == 128) return launch_bwd<DkdvCfg<128, 4, 32, 1>, DqCfg<128, 4, 64, 1>>(variant, p, B, H, st);
+  if (D == 64) return launch_bwd<DkdvCfg<64, 4, 64, 2>, DqCfg<64, 4, 64, 2>>(variant, p, B, H, st);
+  if (D == 128) return launch_bwd<DkdvCfg<128, 4, 64, 1>, DqCfg<128, 4, 64, 2>>(variant, p, B, H, st);
   return hipErrorInvalidValue;
 }
 

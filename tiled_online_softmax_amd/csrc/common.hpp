@@ -121,6 +121,21 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
 }
 
+// Tile offset of the 8 bytes this lane reads with lds_read_tr16 when building
+// the A operand X^T of a 32x32x16 MFMA from a row-major tile X (RB bytes per
+// row): output rows are the 32 columns 32e.. of X, the contraction runs over 16
+// rows of X, and slots 4u..4u+3 come from one read. CL selects the row order
+// of those slots: CL = true gives X rows 8u + 4h + i (the order in which a 32x32
+// accumulator lane holds its rows, h = lane / 32), CL = false gives 8h + 4u + i.
+// Further 16-row contraction chunks add 16 * RB bytes.
+template <int RB, bool CL>
+__device__ __forceinline__ uint32_t tr16_off(int lane, int e, int u) {
+  const int j = lane & 15, g = lane >> 4, h = g >> 1;
+  const int row = CL ? (8 * u + 4 * h + (j >> 2)) : (8 * h + 4 * u + (j >> 2));
+  const int chunk = 4 * e + 2 * (g & 1) + ((j & 3) >> 1);
+  return tile_off<RB>(row, chunk) + 8 * (j & 1);
+}
+
 // vmcnt(0): all of this wave's vector-memory operations (incl. LDS DMA) done.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 

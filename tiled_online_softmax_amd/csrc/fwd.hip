@@ -351,7 +351,6 @@ fwd_kernel(FwdParams P) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int li = lane & 31, hf = lane >> 5;
-  const int j16 = lane & 15, g16 = lane >> 4;
 
   // Workgroup -> (head, query tile); see the staged kernel for the XCD regrouping.
   const int G = gridDim.x;
@@ -410,8 +409,7 @@ fwd_kernel(FwdParams P) {
     for (int e = 0; e < NE; ++e)
 #pragma unroll
       for (int u = 0; u < 2; ++u)
-        voff[e][u] = tile_off<RB>(8 * u + 4 * (g16 >> 1) + (j16 >> 2), 4 * e + 2 * (g16 & 1) + ((j16 & 3) >> 1)) +
-                     8 * (j16 & 1);
+        voff[e][u] = tr16_off<RB, true>(lane, e, u);
   }
 
   f32x16 acc[NE];

@@ -37,7 +37,7 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;     // [B,H,N] workspace: rowsum(dO * O)
+  float* ld;        // [B,H,N,2] workspace: (lse * log2(e), rowsum(dO * O)) per row
   float* dq_accum;  // [B,H,N,D] float workspace (atomic variant), else nullptr
   int N;
   int causal;
