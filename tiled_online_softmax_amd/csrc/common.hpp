@@ -43,25 +43,6 @@ __device__ __forceinline__ float buf_load4f(__amdgpu_buffer_rsrc_t r, uint32_t o
 }
 
 // ---------------------------------------------------------------------------
-// LDS tile layout. A tile is `rows` rows of `RB` bytes, addressed in 16-byte
-// chunks. The chunk index is XOR-swizzled with a function of the row so that
-// 16 lanes reading the same chunk column of 16 consecutive rows hit 16
-// different 16-byte bank groups (64 banks x 4 bytes = one 256-byte line).
-// ---------------------------------------------------------------------------
-template <int RB>
-__device__ __forceinline__ constexpr uint32_t lds_off(int row, int chunk) {
-  constexpr int CPR = RB / 16;  // chunks per row
-  int swz = 0;
-  if constexpr (CPR >= 16) {
-    swz = row & 15;
-  } else {
-    constexpr int RPL = 16 / CPR;  // rows per 256-byte line
-    swz = (row / RPL) & (CPR - 1);
-  }
-  return (uint32_t)(row * RB + ((chunk ^ swz) * 16));
-}
-
-// ---------------------------------------------------------------------------
 // Row-major LDS tiles written by direct global->LDS loads.
 //
 // A tile holds rows of RB bytes, viewed as 256-byte lines (64 banks x 4 B)
@@ -81,12 +62,14 @@ __device__ __forceinline__ constexpr int swz8(int x) { return ((x & 1) << 2) | (
 
 template <int RB>
 __device__ __forceinline__ constexpr uint32_t tile_off(int row, int chunk) {
-  static_assert(RB == 128 || RB % 256 == 0, "row size");
+  static_assert(RB == 64 || RB == 128 || RB % 256 == 0, "row size");
   if constexpr (RB >= 256) {
     constexpr int LPR = RB / 256;  // lines per row
     return (uint32_t)((row * LPR + (chunk >> 4)) * 256 + (((chunk & 15) ^ swz16(row & 15)) << 4));
-  } else {
+  } else if constexpr (RB == 128) {
     return (uint32_t)((row >> 1) * 256 + (((row & 1) << 3) + ((chunk & 7) ^ swz8((row >> 1) & 7))) * 16);
+  } else {
+    return (uint32_t)((row >> 2) * 256 + (((row & 3) << 2) + ((chunk & 3) ^ ((row >> 2) & 3))) * 16);
   }
 }
 
@@ -98,9 +81,12 @@ __device__ __forceinline__ void tile_pos(int phys, int& row, int& chunk) {
     constexpr int LPR = RB / 256;
     row = line / LPR;
     chunk = (line % LPR) * 16 + (pos ^ swz16(row & 15));
-  } else {
+  } else if constexpr (RB == 128) {
     row = 2 * line + (pos >> 3);
     chunk = (pos & 7) ^ swz8(line & 7);
+  } else {
+    row = 4 * line + (pos >> 2);
+    chunk = (pos & 3) ^ (line & 3);
   }
 }
 
@@ -136,6 +122,27 @@ __device__ __forceinline__ uint32_t tr16_off(int lane, int e, int u) {
   return tile_off<RB>(row, chunk) + 8 * (j & 1);
 }
 
+// Transposing 8-byte LDS read of 8-bit elements (gfx950). Within each group
+// of 16 lanes, lane j supplies the address of 8 consecutive bytes M[j][0..7];
+// lane j' receives M[2i + j'/8][j' % 8] for i = 0..7.
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+__device__ __forceinline__ i32x2 lds_read_tr8(const char* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p));
+}
+
+// Tile offset of the 8 bytes this lane reads with lds_read_tr8 for the A
+// operand V^T of a 32x32x64 fp8 MFMA from a row-major tile V (RB bytes per
+// row): output rows are the 32 columns 32e.. of V, and read w (0..3) fills
+// slots 8w..8w+7, which hold V rows 16w + 8(i/4) + 4h + i%4 (i = 0..7) -- the
+// order in which two 32x32 accumulator blocks hold their rows. Further reads
+// w add 16 * RB bytes, further 64-row chunks 64 * RB.
+template <int RB>
+__device__ __forceinline__ uint32_t tr8_off(int lane, int e) {
+  const int j = lane & 15, g = lane >> 4, h = g >> 1;
+  const int row = 8 * (j >> 3) + 4 * h + ((j >> 1) & 3);
+  return tile_off<RB>(row, 2 * e + (g & 1)) + 8 * (j & 1);
+}
+
 // vmcnt(0): all of this wave's vector-memory operations (incl. LDS DMA) done.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -143,28 +150,6 @@ __device__ __forceinline__ float dot2_bf16_sum(int packed_pair, float acc) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed_pair), one, acc, false);
-}
-
-// ---------------------------------------------------------------------------
-// Key permutations for operands read transposed from LDS.
-//
-// The 32x32 MFMA accumulator puts element (r, c) of a block in lane
-// c + 32*((r/4)%2), register (r/8)*4 + r%4. So a lane holding column c holds
-// rows {8a + 4h + t : a = 0..3, t = 0..3} with h = lane/32. When that
-// accumulator (probabilities over keys r) becomes the B operand of the next
-// product, lane-half h supplies keys 8a + 4h + t. The A operand, read from a
-// transposed LDS copy, must list its keys in the same order; storing key j at
-// position perm(j) makes that a contiguous 16-byte (bf16) or 32-byte (fp8)
-// read.
-// ---------------------------------------------------------------------------
-// bf16: a 16-key contraction chunk; swap bits 2 and 3 of the key.
-__device__ __forceinline__ constexpr int perm16(int j) {
-  return (j & ~15) | (((j >> 2) & 1) << 3) | (((j >> 3) & 1) << 2) | (j & 3);
-}
-// fp8: a 64-key contraction chunk made of two 32-key accumulator blocks:
-// key bits [b5 | b4 b3 | b2 | b1 b0] -> position bits [b2 | b5 | b4 b3 | b1 b0].
-__device__ __forceinline__ constexpr int perm64(int j) {
-  return (j & ~63) | (((j >> 2) & 1) << 5) | (((j >> 5) & 1) << 4) | (((j >> 3) & 3) << 2) | (j & 3);
 }
 
 // ---------------------------------------------------------------------------
