@@ -10,9 +10,18 @@ Also reported, each timed on its own with HIP events on the launch stream:
 every other workload's headline pass (the float32 single head, the D=256
 forward, the causal backward, the long-context FP8 forward), the roofline of
 the dominant kernel, and the float64 oracle timed on the host cores on a
-bounded sample of the same workload.
+sample of the same workload.
+
+The dominant kernel is the backward's key-tile pass (dK, dV); it is timed
+alone through fa_bwd_dkdv (preprocess + key-tile kernel) and credited with
+the four contractions it performs (S, dP, dV, dK): 8*B*H*N^2*D flops, halved
+for causal. Its HBM traffic comes from rocprofv3 FETCH_SIZE / WRITE_SIZE
+counters recorded in profiles/traffic_bwd_dkdv.json, scaled by the same
+counters' reading for a plain copy kernel of known size (--calibrate-copy);
+it is reported only while the kernel sources still hash to the recorded value.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-breakdown]
+       python bench.py --calibrate-copy    (plain 512 MiB device copy, for counter calibration)
 """
 from __future__ import annotations
 
@@ -39,7 +48,50 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
     return ap.parse_args()
+
+
+KERNEL_SOURCES = ("tiled_online_softmax_amd/csrc/bwd.hip", "tiled_online_softmax_amd/csrc/common.hpp")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_bwd_dkdv.json")
+
+
+def sources_sha256():
+    """Hash of the dominant kernel's sources with comments and blank lines removed (code changes only)."""
+    import hashlib
+    import re
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f)) as fh:
+            text = re.sub(r"//[^\n]*", "", fh.read())
+        h.update("\n".join(l.rstrip() for l in text.splitlines() if l.strip()).encode())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the dK/dV pass from the committed counter record, or None if stale."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != sources_sha256():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def calibrate_copy():
+    """A plain device copy of known size; its FETCH/WRITE counters calibrate the traffic figures."""
+    import torch
+
+    n = 512 * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 3}), flush=True)
 
 
 def log(*a):
@@ -124,8 +176,8 @@ def breakdown():
     return res
 
 
-def cpu_baseline(w, step_flops):
-    """The float64 oracle on a bounded sample (2 heads, forward + backward), scaled to TFLOP/s."""
+def cpu_baseline(w, step_flops, heads=None):
+    """The float64 oracle on a sample of the step workload (forward + backward of `heads` heads), in TFLOP/s."""
     from oracle import attention, codecs
     from tiled_online_softmax_amd import inputs
 
@@ -135,7 +187,7 @@ def cpu_baseline(w, step_flops):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
-    heads = 2
+    heads = w.B * w.H if heads is None else heads
     d = inputs.make(w, with_grad=True, shape=(1, heads, w.N, w.D))
     q, k, v, do = (codecs.bf16_to_f64(d[n + "_bits"]) for n in ("q", "k", "v", "do"))
     t0 = time.perf_counter()
@@ -151,6 +203,9 @@ def cpu_baseline(w, step_flops):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
               file=sys.stderr)
@@ -193,20 +248,29 @@ def main():
     value = step_flops / (ms * 1e-3) / 1e12
     log(f"[step] {ms:.4f} ms/step, {value:.1f} TFLOP/s")
 
-    # dominant kernel: time forward and backward launches separately
+    # forward and backward passes separately, and the dominant kernel (the backward's
+    # key-tile pass: preprocess + dK/dV kernel) alone through fa_bwd_dkdv
     ms_f = time_fn(fwd, 100)
     ms_b = time_fn(bwd, 100)
     fwd_tf = w.fwd_flops() / (ms_f * 1e-3) / 1e12
     bwd_tf = w.bwd_flops() / (ms_b * 1e-3) / 1e12
-    log(f"[fwd] {ms_f:.4f} ms {fwd_tf:.1f} TF/s   [bwd] {ms_b:.4f} ms {bwd_tf:.1f} TF/s")
-    if ms_b >= ms_f:
-        dom = {"kernel": "backward (fa_bwd, deterministic: delta + dK/dV + dQ kernels)", "ms": ms_b, "tf": bwd_tf,
-               "flops": w.bwd_flops()}
-    else:
-        dom = {"kernel": "fa_fwd kernel", "ms": ms_f, "tf": fwd_tf, "flops": w.fwd_flops()}
-    roofline = {"bound": "mfma", "achieved": round(dom["tf"], 2), "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
-                "frac": round(dom["tf"] / PEAK_TFLOPS["bf16"], 4), "traffic": None, "kernel": dom["kernel"],
-                "avg_launch_ms": round(dom["ms"], 5), "algorithmic_flops_per_launch": dom["flops"]}
+    dk2, dv2 = torch.empty_like(x["q"]), torch.empty_like(x["q"])
+    ws_d = torch.empty(fa.bwd_workspace_size(w.B, w.H, w.N, w.D, fa.FA_BWD_DETERMINISTIC), dtype=torch.uint8,
+                       device="cuda:0")
+
+    def dkdv():
+        fa.bwd_dkdv(x["q"], x["k"], x["v"], o, x["do"], lse, causal=w.causal, workspace=ws_d, dk=dk2, dv=dv2)
+
+    ms_k = time_fn(dkdv, 100)
+    kflops = 8.0 * w.B * w.H * w.N * w.N * w.D / (2 if w.causal else 1)
+    k_tf = kflops / (ms_k * 1e-3) / 1e12
+    log(f"[fwd] {ms_f:.4f} ms {fwd_tf:.1f} TF/s   [bwd] {ms_b:.4f} ms {bwd_tf:.1f} TF/s   "
+        f"[dK/dV pass] {ms_k:.4f} ms {k_tf:.1f} TF/s")
+    roofline = {"bound": "mfma", "achieved": round(k_tf, 2), "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+                "frac": round(k_tf / PEAK_TFLOPS["bf16"], 4), "traffic": recorded_traffic(),
+                "kernel": "backward key-tile pass (bwd_pre_kernel + bwd_dkdv_kernel, via fa_bwd_dkdv)",
+                "avg_launch_ms": round(ms_k, 5), "algorithmic_flops_per_launch": kflops,
+                "traffic_unit": "HBM bytes per launch"}
 
     out = {"metric": "attention fwd/bwd TFLOP/s on 1 MI355X + % of bf16/fp8 MFMA peak", "value": round(value, 2),
            "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

@@ -8,11 +8,11 @@
  *     lse_i = ln sum_j exp(s_ij)              (natural log)
  * computed without materialising the N x N score matrix: K/V are walked in
  * tiles, a running row max and sum are kept, and the output is normalised
- * once at the end. The pages describe this as the "tiled online softmax"
- * baseline (page "r/mlscaling", FA1 bullet), with query-tile ownership and
+ * once at the end. The pages give tiling with an online softmax as the
+ * FA1 baseline (page "r/mlscaling", FA1 bullet), with query-tile ownership and
  * deferred normalisation (FA2 bullet), ping-pong tile buffers and an FP8
  * forward (FA3 bullet), and conditional rescaling (FA4 bullet), all keeping
- * the same exact attention math (closing sentence of that list). The backward
+ * the exact attention result (closing sentence of that list). The backward
  * recomputes the probabilities from lse instead of storing them; the pages
  * name both the atomics-based backward of FlashAttention-2 and an
  * atomics-free alternative that spends more matrix multiplies ("FlashAttention
@@ -154,6 +154,17 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const void* dO, const float* lse, void* dq, void* dk, void* dv,
            int B, int H, int N, int D, int causal, float scale, int dtype,
            int variant, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * dK and dV only: the preprocess and the key-tile pass of fa_bwd, without any
+ * dQ work, for callers that need no gradient with respect to Q. Arguments as
+ * for fa_bwd (dq is not taken); the workspace is the FA_BWD_DETERMINISTIC
+ * size. The results are bitwise those of fa_bwd.
+ */
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* o,
+                const void* dO, const float* lse, void* dk, void* dv,
+                int B, int H, int N, int D, int causal, float scale, int dtype,
+                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static text for a status code. */
 const char* fa_status_string(int status);

@@ -8,8 +8,8 @@ from the HIP path: the two share only the seeded input generator, which
 holds no attention arithmetic.
 
 What it follows. The pages describe FlashAttention FA1-FA4 as orchestrations
-that keep "the same exact attention math" (page "r/mlscaling", the post on an
-educational FA1-FA4 PyTorch repo, closing sentence of the version list). The
+that leave the exact attention result unchanged (page "r/mlscaling", the post
+on an educational FA1-FA4 PyTorch repo, closing sentence of the version list). The
 oracle is therefore that exact math written out: the full score matrix is
 materialised, masked, and normalised with an ordinary softmax -- no tiling,
 no online rescaling.

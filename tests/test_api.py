@@ -138,3 +138,13 @@ def test_error_string_is_per_thread():
     t.join()
     assert seen["msg"] == ""
     assert fa.last_error() != ""
+
+
+def test_bwd_dkdv_validation():
+    L = fa.lib()
+    args = [P] * 8 + [1, 1, 16, 64, 0, 0.125]
+    assert L.fa_bwd_dkdv(*args, fa.FA_F32, P, 1 << 20, None) == fa.FA_ERR_UNSUPPORTED
+    assert L.fa_bwd_dkdv(*args, fa.FA_BF16, None, 1 << 20, None) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_bwd_dkdv(*args, fa.FA_BF16, P, 8, None) == fa.FA_ERR_WORKSPACE
+    bad = [P] * 7 + [None] + [1, 1, 16, 64, 0, 0.125]
+    assert L.fa_bwd_dkdv(*bad, fa.FA_BF16, P, 1 << 20, None) == fa.FA_ERR_INVALID_ARG

@@ -95,3 +95,15 @@ def test_variants_agree():
     # dK and dV come from the same key-tile pass: identical; dQ differs only by summation order
     assert max_abs(ga[1], gd[1]) == 0.0 and max_abs(ga[2], gd[2]) == 0.0
     assert max_abs(ga[0], gd[0]) <= 1e-2
+
+
+def test_dkdv_only_matches_full_backward():
+    """fa_bwd_dkdv returns bitwise the dK, dV of fa_bwd."""
+    dev, _ = prepare("bf16", (2, 3, 700, 128), 21, with_grad=True)
+    for causal in (False, True):
+        o, lse = fa.fwd(dev["q"], dev["k"], dev["v"], causal=causal)
+        _, dk, dv = fa.bwd(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, causal=causal,
+                           variant=fa.FA_BWD_DETERMINISTIC)
+        dk2, dv2 = fa.bwd_dkdv(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(dk, dk2) and torch.equal(dv, dv2)

@@ -126,19 +126,28 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int D, int dtype, int variant)
   return bytes;
 }
 
-int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse, void* dq,
-           void* dk, void* dv, int B, int H, int N, int D, int causal, float scale, int dtype, int variant,
-           void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by fa_bwd and fa_bwd_dkdv; variant 2 is the dK/dV-only pass.
+int bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse, void* dq,
+             void* dk, void* dv, int B, int H, int N, int D, int causal, float scale, int dtype, int variant,
+             void* workspace, size_t workspace_bytes, void* stream) {
   if (dtype != FA_BF16) {
     if (!dtype_bytes(dtype)) return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
     return fail(FA_ERR_UNSUPPORTED, "backward is built for FA_BF16 only (got dtype %d)", dtype);
   }
   if (int s = check_common(B, H, N, D, causal, scale, 2)) return s;
-  if (variant != FA_BWD_ATOMIC && variant != FA_BWD_DETERMINISTIC)
+  if (variant != FA_BWD_ATOMIC && variant != FA_BWD_DETERMINISTIC && variant != 2)
     return fail(FA_ERR_INVALID_ARG, "variant must be FA_BWD_ATOMIC or FA_BWD_DETERMINISTIC (got %d)", variant);
-  if (int s = check_ptrs({q, k, v, o, dO, lse, dq, dk, dv, workspace})) return s;
+  if (variant == 2) {
+    if (int s = check_ptrs({q, k, v, o, dO, lse, dk, dv, workspace})) return s;
+  } else {
+    if (int s = check_ptrs({q, k, v, o, dO, lse, dq, dk, dv, workspace})) return s;
+  }
   if (!fa::bwd_supported(D)) return fail(FA_ERR_UNSUPPORTED, "backward: D=%d is not in the parameter table", D);
-  const size_t need = fa_bwd_workspace_size(B, H, N, D, dtype, variant);
+  const size_t need = fa_bwd_workspace_size(B, H, N, D, dtype, variant == 2 ? FA_BWD_DETERMINISTIC : variant);
   if (workspace_bytes < need) return fail(FA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   fa::BwdParams p{};
   p.q = q; p.k = k; p.v = v; p.o = o; p.dO = dO; p.lse = lse;
@@ -150,6 +159,26 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
                    : nullptr;
   p.N = N; p.causal = causal; p.scale = scale; p.scale_log2 = scale * fa::kLog2e;
   return hip_status(fa::bwd_dispatch(D, variant, p, B, H, reinterpret_cast<hipStream_t>(stream)), "fa_bwd launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse, void* dq,
+           void* dk, void* dv, int B, int H, int N, int D, int causal, float scale, int dtype, int variant,
+           void* workspace, size_t workspace_bytes, void* stream) {
+  if (variant != FA_BWD_ATOMIC && variant != FA_BWD_DETERMINISTIC)
+    return fail(FA_ERR_INVALID_ARG, "variant must be FA_BWD_ATOMIC or FA_BWD_DETERMINISTIC (got %d)", variant);
+  return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, D, causal, scale, dtype, variant, workspace,
+                  workspace_bytes, stream);
+}
+
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                void* dk, void* dv, int B, int H, int N, int D, int causal, float scale, int dtype, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  return bwd_impl(q, k, v, o, dO, lse, nullptr, dk, dv, B, H, N, D, causal, scale, dtype, 2, workspace,
+                  workspace_bytes, stream);
 }
 
 const char* fa_status_string(int status) {

@@ -7,7 +7,8 @@
 // (README, section "Documentation"):
 //   * atomic: one pass over key tiles computes dK and dV and adds each key
 //     tile's dQ contribution into a float32 scratch buffer with atomics
-//     (FlashAttention-2's "scratch space for atomics and partial sums");
+//     (FlashAttention-2 keeps scratch memory for those atomics and partial
+//     sums);
 //   * deterministic: the same key-tile pass for dK and dV, plus a second pass
 //     over query tiles that recomputes S and dP to form dQ -- 7 matrix
 //     products instead of 5 and no atomics, parallel over both rows and
@@ -76,8 +77,6 @@ __global__ void __launch_bounds__(256) bwd_dq_convert_kernel(const float* __rest
   *reinterpret_cast<bf16x8*>(dq + 8 * i) = r;
 }
 
-template <int S> struct BStage { static constexpr int value = S; };
-
 // ---------------------------------------------------------------------------
 // Key-tile pass: dK, dV (and, for the atomic variant, dQ by float atomics).
 // ---------------------------------------------------------------------------
@@ -144,8 +143,7 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
     tile_pos<RB>((wave * C::LPW + i) * 64 + lane, row, ch);
     goff[i] = (uint32_t)(row * RB + ch * 16);
   }
-  auto issue = [&](int q0, int stage) {
-    char* st = smem + stage * C::STAGE;
+  auto issue = [&](int q0, char* st) {
     const uint32_t base = (uint32_t)q0 * RB;
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i) {
@@ -189,16 +187,20 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
   const int nq = (N + BQ - 1) / BQ;
   const float sl2 = P.scale_log2;
 
-  issue(qt0 * BQ, 0);
+  issue(qt0 * BQ, smem);
   wait_vmem();
   __syncthreads();
 
-  auto tile = [&](int it, auto stage_tag) {
-    constexpr int S = decltype(stage_tag)::value;
+  // One query tile. `cur` is read while the LDS-DMA prefetch fills `nxt`; the
+  // restrict qualifiers (also on the dS^T and K tiles) tell the compiler these
+  // regions are disjoint, so it does not wait for the prefetch before reading
+  // them. The prefetch is waited for explicitly at the end of the tile.
+  auto tile = [&](int it, const char* __restrict__ cur, char* __restrict__ nxt, char* __restrict__ dsb,
+                  const char* __restrict__ ktb) {
     const int q0 = it * BQ;
     const bool more = it + 1 < nq;
-    if (more) issue(q0 + BQ, S ^ 1);
-    const char* qs = smem + S * C::STAGE;
+    if (more) issue(q0 + BQ, nxt);
+    const char* qs = cur;
     const char* dos = qs + C::OFF_DO;
     const float* lds_ld = reinterpret_cast<const float*>(qs + C::OFF_LD);
 
@@ -271,7 +273,7 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
           bf16x4 x4;
 #pragma unroll
           for (int t = 0; t < 4; ++t) x4[t] = live ? (__bf16)dp[a][4 * g + t] : (__bf16)0.f;
-          *reinterpret_cast<bf16x4*>(ds_lds + tile_off<C::RB_DS>(kr, 4 * a + g) + 8 * hf) = x4;
+          *reinterpret_cast<bf16x4*>(dsb + tile_off<C::RB_DS>(kr, 4 * a + g) + 8 * hf) = x4;
         }
       __syncthreads();
       // dQ tile (BQ x D) += dS K over this workgroup's BK keys; one 32x32 block per wave per step.
@@ -280,10 +282,10 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
         f32x16 c = f32x16{};
 #pragma unroll
         for (int kc = 0; kc < C::BK / 16; ++kc) {
-          const s16x4 x[2] = {lds_read_tr16(ds_lds + tr16_off<C::RB_DS, false>(lane, a, 0) + kc * 16 * C::RB_DS),
-                              lds_read_tr16(ds_lds + tr16_off<C::RB_DS, false>(lane, a, 1) + kc * 16 * C::RB_DS)};
-          const s16x4 y[2] = {lds_read_tr16(kt_lds + tr16_off<RB, false>(lane, e, 0) + kc * 16 * RB),
-                              lds_read_tr16(kt_lds + tr16_off<RB, false>(lane, e, 1) + kc * 16 * RB)};
+          const s16x4 x[2] = {lds_read_tr16(dsb + tr16_off<C::RB_DS, false>(lane, a, 0) + kc * 16 * C::RB_DS),
+                              lds_read_tr16(dsb + tr16_off<C::RB_DS, false>(lane, a, 1) + kc * 16 * C::RB_DS)};
+          const s16x4 y[2] = {lds_read_tr16(ktb + tr16_off<RB, false>(lane, e, 0) + kc * 16 * RB),
+                              lds_read_tr16(ktb + tr16_off<RB, false>(lane, e, 1) + kc * 16 * RB)};
           c = mfma_bf16(__builtin_bit_cast(bf16x8, x), __builtin_bit_cast(bf16x8, y), c);
         }
         float* dst = P.dq_accum + ((size_t)bh * N) * D + 32 * e + li;
@@ -299,8 +301,8 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
     __syncthreads();
   };
   for (int it = qt0; it < nq; it += 2) {
-    tile(it, BStage<0>{});
-    if (it + 1 < nq) tile(it + 1, BStage<1>{});
+    tile(it, smem, smem + C::STAGE, ds_lds, kt_lds);
+    if (it + 1 < nq) tile(it + 1, smem + C::STAGE, smem, ds_lds, kt_lds);
   }
 
   if (key < N) {
@@ -386,8 +388,7 @@ bwd_dq_kernel(BwdParams P, int n_qtiles) {
     tile_pos<RB>((wave * C::LPW + i) * 64 + lane, row, ch);
     goff[i] = (uint32_t)(row * RB + ch * 16);
   }
-  auto issue = [&](int key0, int stage) {
-    char* kb = smem + stage * C::STAGE;
+  auto issue = [&](int key0, char* kb) {
     const uint32_t base = (uint32_t)key0 * RB;
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i) {
@@ -412,16 +413,16 @@ bwd_dq_kernel(BwdParams P, int n_qtiles) {
   const int kv_end = P.causal ? min(N, q0 + C::BM) : N;
   const int n_tiles = (kv_end + BN - 1) / BN;
 
-  issue(0, 0);
+  issue(0, smem);
   wait_vmem();
   __syncthreads();
 
-  auto tile = [&](int t, auto stage_tag) {
-    constexpr int S = decltype(stage_tag)::value;
+  // One key tile; see the key-tile pass for the restrict qualifiers.
+  auto tile = [&](int t, const char* __restrict__ cur, char* __restrict__ nxt) {
     const int key0 = t * BN;
     const bool more = t + 1 < n_tiles;
-    if (more) issue(key0 + BN, S ^ 1);
-    const char* ks = smem + S * C::STAGE;
+    if (more) issue(key0 + BN, nxt);
+    const char* ks = cur;
     const char* vs = ks + C::TILE;
     if (!P.causal || key0 <= qw + 31) {
       f32x16 s[NB], dp[NB];
@@ -466,8 +467,8 @@ bwd_dq_kernel(BwdParams P, int n_qtiles) {
     __syncthreads();
   };
   for (int t = 0; t < n_tiles; t += 2) {
-    tile(t, BStage<0>{});
-    if (t + 1 < n_tiles) tile(t + 1, BStage<1>{});
+    tile(t, smem, smem + C::STAGE);
+    if (t + 1 < n_tiles) tile(t + 1, smem + C::STAGE, smem);
   }
 
   if (qrow < N) {
@@ -511,6 +512,7 @@ static hipError_t launch_bwd(int variant, const BwdParams& p, int B, int H, hipS
   }
   hipLaunchKernelGGL((bwd_dkdv_kernel<KC, false>), dim3((unsigned)gk), dim3(KC::NT), 0, st, p, nk);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (variant == 2) return hipSuccess;  // dK/dV only
   const int nq = (p.N + QC::BM - 1) / QC::BM;
   const long long gq = (long long)nq * B * H;
   if (gq > 0x7fffffffLL) return hipErrorInvalidConfiguration;

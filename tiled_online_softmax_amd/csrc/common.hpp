@@ -166,9 +166,17 @@ __device__ __forceinline__ f32x16 mfma_f32(float a, float b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-// Exchange with the lane 32 away (the other half of a 32x32 block column).
-__device__ __forceinline__ float xor32(float x) {
-  return __shfl_xor(x, 32, 64);
+// Combine a value with the one held by the lane 32 away (the other half of a
+// 32x32 accumulator column), with v_permlane32_swap: swapping the upper half
+// of one copy with the lower half of another leaves, in every lane, its own
+// value in one result and its partner's in the other.
+__device__ __forceinline__ float pair_max32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ bool wave_any(bool p) {

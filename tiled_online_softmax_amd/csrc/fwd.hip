@@ -54,8 +54,6 @@ struct FwdDCfg {
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-template <int S> struct StageTag { static constexpr int value = S; };
-
 template <class C>
 __global__ void __launch_bounds__(C::NT)
 __attribute__((amdgpu_waves_per_eu(C::OCC, C::OCC)))
@@ -111,8 +109,7 @@ fwd_kernel(FwdParams P) {
     tile_pos<RB>((wave * C::LPW + i) * 64 + lane, row, ch);
     goff[i] = (uint32_t)(row * RB + ch * 16);
   }
-  auto issue = [&](int key0, int stage) {
-    char* kb = smem + stage * C::STAGE;
+  auto issue = [&](int key0, char* kb) {
     const uint32_t base = (uint32_t)key0 * RB;
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i) {
@@ -151,60 +148,89 @@ fwd_kernel(FwdParams P) {
   const int kv_end = P.causal ? min(N, q0 + C::BM) : N;
   const int n_tiles = (kv_end + BN - 1) / BN;
 
-  issue(0, 0);
+  issue(0, smem);
   wait_vmem();
   __syncthreads();
 
-  auto tile = [&](int t, auto stage_tag) {
-    constexpr int S = decltype(stage_tag)::value;
+  // One key/value tile. `cur` (being read) and `nxt` (being filled by the
+  // LDS-DMA prefetch) are distinct stage buffers; declaring them restrict lets
+  // the compiler see that the transposing reads of `cur` cannot depend on the
+  // prefetch, so it does not wait for the prefetch before them. The prefetch is
+  // waited for explicitly (vmcnt + barrier) at the end of the tile.
+  auto tile = [&](int t, const char* __restrict__ cur, char* __restrict__ nxt) {
     const int key0 = t * BN;
     const bool more = (t + 1) < n_tiles;
-    if (more) issue(key0 + BN, S ^ 1);
-    const char* ks = smem + S * C::STAGE;
-    const char* vs = ks + C::TILE;
+    if (more) issue(key0 + BN, nxt);
+    const char* ks = cur;
+    const char* vs = cur + C::TILE;
     if (!P.causal || key0 <= qw + 31) {
       // ---- S^T = K Q^T ----
+      // K operands are read KLA pieces ahead into a register ring: the reads
+      // for piece p+KLA are issued before the MFMAs of piece p (scheduling
+      // barriers keep that order), so LDS latency hides behind KLA*NB MFMAs.
       f32x16 s[NB];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        s[b] = f32x16{};
+      for (int b = 0; b < NB; ++b) s[b] = f32x16{};
+      if constexpr (C::elt == Elt::BF16) {
+        constexpr int KLA = 2;
+        i32x4 ka[KLA + 1][NB];
+#pragma unroll
+        for (int p = 0; p < KLA; ++p)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) ka[p][b] = *reinterpret_cast<const i32x4*>(ks + koff[p] + 32 * b * RB);
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-          if constexpr (C::elt == Elt::BF16) {
-            const i32x4 a = *reinterpret_cast<const i32x4*>(ks + koff[p] + 32 * b * RB);
-            s[b] = mfma_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qf[p]), s[b]);
-          } else if constexpr (C::elt == Elt::FP8) {
-            if (p & 1) continue;  // one MFMA per pair of 16-byte pieces (64 fp8 values)
-            const i32x4 a0 = *reinterpret_cast<const i32x4*>(ks + koff[p] + 32 * b * RB);
-            const i32x4 a1 = *reinterpret_cast<const i32x4*>(ks + koff[p + 1] + 32 * b * RB);
-            const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-            const i32x8 bq = {qf[p][0], qf[p][1], qf[p][2], qf[p][3],
-                              qf[p + 1][0], qf[p + 1][1], qf[p + 1][2], qf[p + 1][3]};
-            s[b] = mfma_fp8(a, bq, s[b]);
-          } else {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(ks + koff[p] + 32 * b * RB);
-            const f32x4 bq = __builtin_bit_cast(f32x4, qf[p]);
+          if (p + KLA < NP) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) s[b] = mfma_f32(a[u], bq[u], s[b]);
+            for (int b = 0; b < NB; ++b)
+              ka[(p + KLA) % (KLA + 1)][b] = *reinterpret_cast<const i32x4*>(ks + koff[p + KLA] + 32 * b * RB);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+            s[b] = mfma_bf16(__builtin_bit_cast(bf16x8, ka[p % (KLA + 1)][b]), __builtin_bit_cast(bf16x8, qf[p]), s[b]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+#pragma unroll
+          for (int p = 0; p < NP; ++p) {
+            if constexpr (C::elt == Elt::FP8) {
+              if (p & 1) continue;  // one MFMA per pair of 16-byte pieces (64 fp8 values)
+              const i32x4 a0 = *reinterpret_cast<const i32x4*>(ks + koff[p] + 32 * b * RB);
+              const i32x4 a1 = *reinterpret_cast<const i32x4*>(ks + koff[p + 1] + 32 * b * RB);
+              const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+              const i32x8 bq = {qf[p][0], qf[p][1], qf[p][2], qf[p][3],
+                                qf[p + 1][0], qf[p + 1][1], qf[p + 1][2], qf[p + 1][3]};
+              s[b] = mfma_fp8(a, bq, s[b]);
+            } else {
+              const f32x4 a = *reinterpret_cast<const f32x4*>(ks + koff[p] + 32 * b * RB);
+              const f32x4 bq = __builtin_bit_cast(f32x4, qf[p]);
+#pragma unroll
+              for (int u = 0; u < 4; ++u) s[b] = mfma_f32(a[u], bq[u], s[b]);
+            }
           }
         }
       }
       // ---- mask (causal diagonal / ragged tail) and tile row max ----
       if ((key0 + BN > N) || (P.causal && key0 + BN - 1 > qw)) {
+        // key index key0 + 32b + 8(v/4) + 4h + v%4 is kept iff <= min(qrow, N-1) (causal)
+        // or <= N-1; compare the lane-independent part against one per-lane limit.
+        const int lim = (P.causal ? min(qrow, N - 1) : N - 1) - key0 - 4 * hf;
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int key = key0 + 32 * b + (v >> 2) * 8 + hf * 4 + (v & 3);
-            if (key >= N || (P.causal && key > qrow)) s[b][v] = -INFINITY;
-          }
+          for (int v = 0; v < 16; ++v)
+            if (32 * b + (v >> 2) * 8 + (v & 3) > lim) s[b][v] = -INFINITY;
       }
-      float mx = -INFINITY;
+      // row max: four independent max3 chains, then the partner lane
+      float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[b][v]);
-      mx = fmaxf(mx, xor32(mx)) * sc;
+        for (int v = 0; v < 16; v += 2) m4[(v >> 1) & 3] = fmaxf(m4[(v >> 1) & 3], fmaxf(s[b][v], s[b][v + 1]));
+      const float mx = pair_max32(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) * sc;
       // ---- conditional rescale ----
       const bool grow = mx > m_ref + tau;
       if (wave_any(grow)) {
@@ -222,8 +248,21 @@ fwd_kernel(FwdParams P) {
         for (int v = 0; v < 16; ++v) s[b][v] = fast_exp2(__builtin_fmaf(s[b][v], sc, neg_m));
       // ---- O^T += V^T P^T ----
       if constexpr (C::elt == Elt::BF16) {
+        // V^T operands double-buffered like K above; four independent row-sum chains.
+        float l4[4] = {0.f, 0.f, 0.f, 0.f};
+        s16x4 va[2][NE][2];
+#pragma unroll
+        for (int e = 0; e < NE; ++e)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) va[0][e][u] = lds_read_tr16(vs + voff[e][u]);
 #pragma unroll
         for (int kc = 0; kc < BN / 16; ++kc) {
+          if (kc + 1 < BN / 16) {
+#pragma unroll
+            for (int e = 0; e < NE; ++e)
+#pragma unroll
+              for (int u = 0; u < 2; ++u) va[(kc + 1) & 1][e][u] = lds_read_tr16(vs + voff[e][u] + (kc + 1) * 16 * RB);
+          }
           const f32x16& sb = s[kc >> 1];
           const int o8 = (kc & 1) * 8;
           bf16x8 pb;
@@ -231,15 +270,14 @@ fwd_kernel(FwdParams P) {
           for (int i = 0; i < 8; ++i) pb[i] = (__bf16)sb[o8 + i];
           const i32x4 pw = __builtin_bit_cast(i32x4, pb);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) l_part = dot2_bf16_sum(pw[i], l_part);
+          for (int i = 0; i < 4; ++i) l4[i] = dot2_bf16_sum(pw[i], l4[i]);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int e = 0; e < NE; ++e) {
-            const s16x4 lo = lds_read_tr16(vs + voff[e][0] + kc * 16 * RB);
-            const s16x4 hi = lds_read_tr16(vs + voff[e][1] + kc * 16 * RB);
-            const s16x4 a8[2] = {lo, hi};
-            acc[e] = mfma_bf16(__builtin_bit_cast(bf16x8, a8), pb, acc[e]);
-          }
+          for (int e = 0; e < NE; ++e)
+            acc[e] = mfma_bf16(__builtin_bit_cast(bf16x8, va[kc & 1][e]), pb, acc[e]);
+          __builtin_amdgcn_sched_barrier(0);
         }
+        l_part += (l4[0] + l4[1]) + (l4[2] + l4[3]);
       } else if constexpr (C::elt == Elt::FP8) {
 #pragma unroll
         for (int kc = 0; kc < BN / 64; ++kc) {
@@ -281,12 +319,12 @@ fwd_kernel(FwdParams P) {
     __syncthreads();
   };
   for (int t = 0; t < n_tiles; t += 2) {
-    tile(t, StageTag<0>{});
-    if (t + 1 < n_tiles) tile(t + 1, StageTag<1>{});
+    tile(t, smem, smem + C::STAGE);
+    if (t + 1 < n_tiles) tile(t + 1, smem + C::STAGE, smem);
   }
 
   // ---- epilogue: O = acc / l, lse = ln(sum exp(s)) ----
-  const float l_tot = l_part + xor32(l_part);
+  const float l_tot = pair_sum32(l_part);
   const float inv = out_mul / l_tot;
   if (qrow < N) {
     const size_t row_base = ((size_t)bh * N + qrow) * D;
@@ -331,7 +369,7 @@ hipError_t fwd_dispatch(Elt e, int D, const FwdParams& p, int B, int H, hipStrea
     case Elt::BF16:
       if (D == 64) return launch_fwd_direct<FwdDCfg<Elt::BF16, 64, 64, 4, 2>>(p, B, H, st);
       if (D == 128) return launch_fwd_direct<FwdDCfg<Elt::BF16, 128, 64, 4, 2>>(p, B, H, st);
-      if (D == 256) return launch_fwd_direct<FwdDCfg<Elt::BF16, 256, 32, 4, 1>>(p, B, H, st);
+      if (D == 256) return launch_fwd_direct<FwdDCfg<Elt::BF16, 256, 64, 4, 1>>(p, B, H, st);
       break;
     case Elt::FP8:
       if (D == 64) return launch_fwd_direct<FwdDCfg<Elt::FP8, 64, 64, 4, 2>>(p, B, H, st);

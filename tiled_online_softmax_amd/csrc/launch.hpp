@@ -46,6 +46,7 @@ struct BwdParams {
 };
 
 bool bwd_supported(int D);
+// variant: 0 atomic, 1 deterministic, 2 dK/dV only (no dQ)
 hipError_t bwd_dispatch(int D, int variant, const BwdParams& p, int B, int H, hipStream_t st);
 
 hipError_t quantize_fp8_launch(const float* x, size_t n, void* codes, float* descale, hipStream_t st);

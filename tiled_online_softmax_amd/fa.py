@@ -22,7 +22,7 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0,
 FA_BWD_ATOMIC, FA_BWD_DETERMINISTIC = 0, 1
 
 EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_fwd_fp8", "fa_quantize_fp8", "fa_bwd_workspace_size", "fa_bwd",
-            "fa_status_string", "fa_last_error")
+            "fa_bwd_dkdv", "fa_status_string", "fa_last_error")
 
 
 class FAError(RuntimeError):
@@ -49,11 +49,12 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd_workspace_size.argtypes = [_i] * 6
         L.fa_bwd_workspace_size.restype = _sz
         L.fa_bwd.argtypes = [_vp] * 9 + [_i] * 5 + [_f, _i, _i, _vp, _sz, _vp]
+        L.fa_bwd_dkdv.argtypes = [_vp] * 8 + [_i] * 5 + [_f, _i, _vp, _sz, _vp]
         L.fa_status_string.argtypes = [_i]
         L.fa_status_string.restype = ctypes.c_char_p
         L.fa_last_error.argtypes = []
         L.fa_last_error.restype = ctypes.c_char_p
-        for name in ("fa_fwd", "fa_fwd_ex", "fa_fwd_fp8", "fa_quantize_fp8", "fa_bwd"):
+        for name in ("fa_fwd", "fa_fwd_ex", "fa_fwd_fp8", "fa_quantize_fp8", "fa_bwd", "fa_bwd_dkdv"):
             getattr(L, name).restype = _i
         _lib = L
     return _lib
@@ -177,3 +178,22 @@ def bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None
                         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, D, int(causal), scale, _dtype_code(q),
                         variant, workspace.data_ptr(), workspace.numel(), _stream(q)))
     return dq, dk, dv
+
+
+def bwd_dkdv(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None,
+             workspace: Optional[torch.Tensor] = None, dk=None, dv=None):
+    """dK and dV only (bf16), the key-tile pass of the backward. Returns (dK, dV)."""
+    _check_qkv(q, k, v, o, do)
+    B, H, N, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if lse.dtype != torch.float32 or lse.shape != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, N]")
+    need = bwd_workspace_size(B, H, N, D, FA_BWD_DETERMINISTIC)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check(lib().fa_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                             dk.data_ptr(), dv.data_ptr(), B, H, N, D, int(causal), scale, _dtype_code(q),
+                             workspace.data_ptr(), workspace.numel(), _stream(q)))
+    return dk, dv
