@@ -125,9 +125,9 @@ int fa_quantize_fp8(const float* x, size_t n, void* codes, float* descale,
                     void* stream);
 
 /*
- * Workspace bytes fa_bwd needs: a float pair per row, (lse_i * log2(e),
- * D_i = sum_d dO_id O_id) [B, H, N, 2], plus a float dQ accumulator
- * [B, H, N, D] for FA_BWD_ATOMIC. 0 on invalid input.
+ * Workspace bytes fa_bwd needs: two floats per row, lse_i * log2(e) and
+ * -D_i with D_i = sum_d dO_id O_id (each [B, H, N]), plus a float dQ
+ * accumulator [B, H, N, D] for FA_BWD_ATOMIC. 0 on invalid input.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int D, int dtype, int variant);
 

@@ -92,8 +92,12 @@ def test_variants_agree():
     dev, _ = prepare("bf16", (1, 2, 900, 128), 6, with_grad=True)
     ga = _grads(dev, True, 0.1, fa.FA_BWD_ATOMIC)
     gd = _grads(dev, True, 0.1, fa.FA_BWD_DETERMINISTIC)
-    # dK and dV come from the same key-tile pass: identical; dQ differs only by summation order
-    assert max_abs(ga[1], gd[1]) == 0.0 and max_abs(ga[2], gd[2]) == 0.0
+    # The variants use different key-pass tilings and query-tile orders, so dK and dV differ only by
+    # the fp32 summation order: at most one bf16 step of the larger value, up to cancellation near zero.
+    for a, b in ((ga[1], gd[1]), (ga[2], gd[2])):
+        a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+        bound = 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b)) + 1e-4 * np.abs(a).max()
+        assert np.all(np.abs(a - b) <= bound)
     assert max_abs(ga[0], gd[0]) <= 1e-2
 
 

@@ -147,6 +147,8 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
     if (int s = check_ptrs({q, k, v, o, dO, lse, dq, dk, dv, workspace})) return s;
   }
   if (!fa::bwd_supported(D)) return fail(FA_ERR_UNSUPPORTED, "backward: D=%d is not in the parameter table", D);
+  if ((unsigned long long)B * H * N * 8ULL >= (1ULL << 32))
+    return fail(FA_ERR_UNSUPPORTED, "backward: B*H*N = %lld rows exceeds the 2^29 rows one call supports", (long long)B * H * N);
   const size_t need = fa_bwd_workspace_size(B, H, N, D, dtype, variant == 2 ? FA_BWD_DETERMINISTIC : variant);
   if (workspace_bytes < need) return fail(FA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   fa::BwdParams p{};
@@ -158,6 +160,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
                    ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + ((rows * 2 * sizeof(float) + 255) & ~(size_t)255))
                    : nullptr;
   p.N = N; p.causal = causal; p.scale = scale; p.scale_log2 = scale * fa::kLog2e;
+  p.rows = (long long)rows;
   return hip_status(fa::bwd_dispatch(D, variant, p, B, H, reinterpret_cast<hipStream_t>(stream)), "fa_bwd launch");
 }
 

@@ -30,8 +30,10 @@ namespace fa {
 constexpr float kInf = __builtin_huge_valf();
 
 // ---------------------------------------------------------------------------
-// ld[row] = (lse * log2(e), D = sum_d dO O) as a float pair; the atomic variant
-// also zeroes dQ_accum. One thread per 8 consecutive elements of a row.
+// Row statistics for the passes: ld[row] = lse * log2(e) and
+// ld[rows + row] = -D with D = sum_d dO O (negated so it can initialise the
+// dP accumulator, which then holds dP - D for free); the atomic variant also
+// zeroes dQ_accum. One thread per 8 consecutive elements of a row.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ dO,
@@ -56,8 +58,8 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const __bf16* __restrict__
 #pragma unroll
   for (int o2 = TPR / 2; o2 > 0; o2 >>= 1) s += __shfl_xor(s, o2, 64);
   if (row < rows && part == 0) {
-    ld[2 * row] = lse[row] * kLog2e;
-    ld[2 * row + 1] = s;
+    ld[row] = lse[row] * kLog2e;
+    ld[rows + row] = -s;
   }
 }
 
@@ -89,7 +91,7 @@ struct DkdvCfg {
   static constexpr int QTILE = BQ * RB; // one Q (or dO) tile
   static constexpr int OFF_DO = QTILE;
   static constexpr int OFF_LD = 2 * QTILE;
-  static constexpr int STAGE = 2 * QTILE + 1024;  // + (lse*log2e, D) pairs, BQ*8 <= 1 KB
+  static constexpr int STAGE = 2 * QTILE + 1024;  // + lse*log2e and -D rows, 2*BQ*4 <= 1 KB
   static constexpr int KTILE = BK * RB;           // K tile (atomic variant)
   static constexpr int RB_DS = BQ * 2;            // dS^T tile: [key][query] bf16
   static constexpr int DSTILE = BK * RB_DS;
@@ -98,7 +100,7 @@ struct DkdvCfg {
   static constexpr int NP = RB / 32;
   static constexpr int NA = BQ / 32, NE = D / 32;
   static_assert(QTILE % (1024 * NW) == 0 && BQ * 8 <= 1024 && BQ % 32 == 0, "tile shape");
-  static_assert(RB_DS == 128 || RB_DS % 256 == 0, "dS tile row");
+  static_assert(RB_DS == 64 || RB_DS == 128 || RB_DS % 256 == 0, "dS tile row");
 };
 
 template <class C, bool ATOMIC>
@@ -108,7 +110,8 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
   constexpr int D = C::D, BQ = C::BQ, NE = C::NE, NA = C::NA, RB = C::RB, NP = C::NP;
   constexpr int SMEM = 2 * C::STAGE + (ATOMIC ? C::KTILE + C::DSTILE : 0);
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 31, hf = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 31, hf = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps per-wave branches scalar
 
   const int G = gridDim.x;
   int w = blockIdx.x;
@@ -126,7 +129,10 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
   const auto rk = make_rsrc(reinterpret_cast<const __bf16*>(P.k) + head, head_bytes);
   const auto rv = make_rsrc(reinterpret_cast<const __bf16*>(P.v) + head, head_bytes);
   const auto rdo = make_rsrc(reinterpret_cast<const __bf16*>(P.dO) + head, head_bytes);
-  const auto rld = make_rsrc(P.ld + (size_t)bh * N * 2, (uint32_t)((size_t)N * 8));
+  // lse*log2e rows of this head, and the -D rows `rows` floats further on
+  const size_t rows = (size_t)P.rows;
+  const auto rld = make_rsrc(P.ld, (uint32_t)(rows * 8));
+  const uint32_t ld_l2 = (uint32_t)((size_t)bh * N * 4), ld_nd = (uint32_t)((rows + (size_t)bh * N) * 4);
 
   // K^T and V^T pieces (B operands of S = Q K^T and dP = dO V^T).
   i32x4 kf[NP], vf[NP];
@@ -151,7 +157,11 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
       buf_load_lds16(rq, goff[i] + base, 0, (lds_void*)(st + m * 1024));
       buf_load_lds16(rdo, goff[i] + base, 0, (lds_void*)(st + C::OFF_DO + m * 1024));
     }
-    if (wave == 0 && lane < BQ / 2) buf_load_lds16(rld, (uint32_t)(q0 * 8 + lane * 16), 0, (lds_void*)(st + C::OFF_LD));
+    // lanes 0..BQ/4-1 bring lse*log2e of the tile's rows, the next BQ/4 lanes their -D
+    if (wave == 0 && lane < BQ / 2) {
+      const int half = lane >= BQ / 4, j = lane - half * (BQ / 4);
+      buf_load_lds16(rld, (half ? ld_nd : ld_l2) + (uint32_t)(q0 * 4 + j * 16), 0, (lds_void*)(st + C::OFF_LD));
+    }
   };
 
   char* kt_lds = smem + 2 * C::STAGE;
@@ -166,15 +176,12 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
     }
   }
 
-  // Per-lane LDS offsets.
-  uint32_t qoff[NP];
-#pragma unroll
-  for (int p = 0; p < NP; ++p) qoff[p] = tile_off<RB>(li, 2 * p + hf);
-  uint32_t troff[NE][2];  // Q^T / dO^T operands, query order of the S accumulator
-#pragma unroll
-  for (int e = 0; e < NE; ++e)
-#pragma unroll
-    for (int u = 0; u < 2; ++u) troff[e][u] = tr16_off<RB, true>(lane, e, u);
+  // Per-lane LDS offsets, one base register per operand kind: piece p of a
+  // row-major Q/dO operand sits at qbase ^ piece_xor(p), transposed piece
+  // (e, u) at tbase ^ tr16_xor(e, u).
+  static_assert(piece_xor_ok<RB, NP>() && tr16_xor_ok<RB, true, NE>(), "offset XOR form");
+  uint32_t qbase = tile_off<RB>(li, hf);
+  uint32_t tbase = tr16_off<RB, true>(lane, 0, 0);
 
   f32x16 adk[NE], adv[NE];
 #pragma unroll
@@ -203,63 +210,95 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
     const char* qs = cur;
     const char* dos = qs + C::OFF_DO;
     const float* lds_ld = reinterpret_cast<const float*>(qs + C::OFF_LD);
+    opaque(qbase);
+    opaque(tbase);
 
     const bool live = !P.causal || q0 + BQ - 1 >= kw;
-    f32x16 s[NA], dp[NA];
+    bf16x8 pb[BQ / 16], db[BQ / 16];  // P and dS as bf16 B operands, 16 queries per piece
     if (live) {
+      f32x16 s[NA], dp[NA];
+      // S = Q K^T and dP = dO V^T. The Q/dO pieces are read LA pieces ahead into
+      // a register ring; scheduling barriers keep the reads ahead of the MFMAs
+      // they feed, so LDS latency hides behind the MFMAs in between.
+      constexpr int LA = D >= 128 ? 1 : 2;
 #pragma unroll
       for (int a = 0; a < NA; ++a) {
         s[a] = f32x16{};
-        dp[a] = f32x16{};
+        // dP accumulator starts at -D of each row, so it ends as dP - D
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 nd = *reinterpret_cast<const f32x4*>(lds_ld + BQ + 32 * a + 8 * g + 4 * hf);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) dp[a][4 * g + t] = nd[t];
+        }
+        i32x4 xq[LA + 1], xd[LA + 1];
+        auto rd = [&](int p) {
+          const uint32_t o = (qbase ^ piece_xor(p)) + 32 * a * RB;
+          xq[p % (LA + 1)] = *reinterpret_cast<const i32x4*>(qs + o);
+          xd[p % (LA + 1)] = *reinterpret_cast<const i32x4*>(dos + o);
+        };
+#pragma unroll
+        for (int p = 0; p < LA; ++p) rd(p);
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-          const i32x4 x = *reinterpret_cast<const i32x4*>(qs + qoff[p] + 32 * a * RB);
-          s[a] = mfma_bf16(__builtin_bit_cast(bf16x8, x), __builtin_bit_cast(bf16x8, kf[p]), s[a]);
-          const i32x4 y = *reinterpret_cast<const i32x4*>(dos + qoff[p] + 32 * a * RB);
-          dp[a] = mfma_bf16(__builtin_bit_cast(bf16x8, y), __builtin_bit_cast(bf16x8, vf[p]), dp[a]);
+          if (p + LA < NP) rd(p + LA);
+          __builtin_amdgcn_sched_barrier(0);
+          s[a] = mfma_bf16(__builtin_bit_cast(bf16x8, xq[p % (LA + 1)]), __builtin_bit_cast(bf16x8, kf[p]), s[a]);
+          dp[a] = mfma_bf16(__builtin_bit_cast(bf16x8, xd[p % (LA + 1)]), __builtin_bit_cast(bf16x8, vf[p]), dp[a]);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-      // P = 2^(s*sl2 - lse*log2e), dS = P (dP - D); accumulator rows are queries 32a + 8g + 4h + t.
-      const bool mask = (P.causal && q0 < kw + 31) || (q0 + BQ > N);
+      // P = 2^(s*sl2 - lse*log2e); accumulator rows are queries 32a + 8g + 4h + t.
 #pragma unroll
       for (int a = 0; a < NA; ++a)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int qb = 32 * a + 8 * g + 4 * hf;
-          const f32x4 x0 = *reinterpret_cast<const f32x4*>(lds_ld + 2 * qb);      // (l2,d) rows qb, qb+1
-          const f32x4 x1 = *reinterpret_cast<const f32x4*>(lds_ld + 2 * qb + 4);  // rows qb+2, qb+3
-          const float l2[4] = {x0[0], x0[2], x1[0], x1[2]};
-          const float dd[4] = {x0[1], x0[3], x1[1], x1[3]};
+          const f32x4 l2 = *reinterpret_cast<const f32x4*>(lds_ld + 32 * a + 8 * g + 4 * hf);
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int v = 4 * g + t;
-            float pv = fast_exp2(__builtin_fmaf(s[a][v], sl2, -l2[t]));
-            if (mask) {
-              const int q = q0 + qb + t;
-              if (q >= N || (P.causal && key > q)) pv = 0.f;
-            }
-            s[a][v] = pv;
-            dp[a][v] = pv * (dp[a][v] - dd[t]);
-          }
+          for (int t = 0; t < 4; ++t) s[a][4 * g + t] = fast_exp2(__builtin_fmaf(s[a][4 * g + t], sl2, -l2[t]));
         }
-      // dV^T += dO^T P ; dK^T += Q^T dS (contraction over 16-query chunks)
+      // Masked tiles (causal diagonal, ragged tail) only; the flag is wave-uniform.
+      if ((P.causal && q0 < kw + 31) || (q0 + BQ > N)) {
 #pragma unroll
-      for (int kc = 0; kc < BQ / 16; ++kc) {
-        bf16x8 pb, db;
+        for (int a = 0; a < NA; ++a)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int q = q0 + 32 * a + 8 * (v >> 2) + 4 * hf + (v & 3);
+            if (q >= N || (P.causal && key > q)) s[a][v] = 0.f;
+          }
+      }
+      // dS = P (dP - D); both to bf16 pieces
+#pragma unroll
+      for (int kc = 0; kc < BQ / 16; ++kc)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          pb[i] = (__bf16)s[kc >> 1][(kc & 1) * 8 + i];
-          db[i] = (__bf16)dp[kc >> 1][(kc & 1) * 8 + i];
+          const float pv = s[kc >> 1][(kc & 1) * 8 + i];
+          pb[kc][i] = (__bf16)pv;
+          db[kc][i] = (__bf16)(pv * dp[kc >> 1][(kc & 1) * 8 + i]);
         }
+
+      // dV^T += dO^T P ; dK^T += Q^T dS, over 16-query chunks kc and 32-column
+      // blocks e; the transposed dO/Q pieces are read one step ahead.
+      constexpr int NS = BQ / 16 * NE;
+      s16x4 tx[2][2], ty[2][2];
+      auto rdt = [&](int st) {
+        const int kc = st / NE, e = st % NE;
 #pragma unroll
-        for (int e = 0; e < NE; ++e) {
-          const s16x4 x[2] = {lds_read_tr16(dos + troff[e][0] + kc * 16 * RB),
-                              lds_read_tr16(dos + troff[e][1] + kc * 16 * RB)};
-          adv[e] = mfma_bf16(__builtin_bit_cast(bf16x8, x), pb, adv[e]);
-          const s16x4 y[2] = {lds_read_tr16(qs + troff[e][0] + kc * 16 * RB),
-                              lds_read_tr16(qs + troff[e][1] + kc * 16 * RB)};
-          adk[e] = mfma_bf16(__builtin_bit_cast(bf16x8, y), db, adk[e]);
+        for (int u = 0; u < 2; ++u) {
+          const uint32_t o = (tbase ^ tr16_xor<RB, true>(e, u)) + kc * 16 * RB;
+          tx[st & 1][u] = lds_read_tr16(dos + o);
+          ty[st & 1][u] = lds_read_tr16(qs + o);
         }
+      };
+      rdt(0);
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const int kc = st / NE, e = st % NE;
+        if (st + 1 < NS) rdt(st + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        adv[e] = mfma_bf16(__builtin_bit_cast(bf16x8, tx[st & 1]), pb[kc], adv[e]);
+        adk[e] = mfma_bf16(__builtin_bit_cast(bf16x8, ty[st & 1]), db[kc], adk[e]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 
@@ -272,7 +311,7 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
         for (int g = 0; g < 4; ++g) {
           bf16x4 x4;
 #pragma unroll
-          for (int t = 0; t < 4; ++t) x4[t] = live ? (__bf16)dp[a][4 * g + t] : (__bf16)0.f;
+          for (int t = 0; t < 4; ++t) x4[t] = live ? db[2 * a + (g >> 1)][4 * (g & 1) + t] : (__bf16)0.f;
           *reinterpret_cast<bf16x4*>(dsb + tile_off<C::RB_DS>(kr, 4 * a + g) + 8 * hf) = x4;
         }
       __syncthreads();
@@ -348,7 +387,8 @@ __attribute__((amdgpu_waves_per_eu(C::OCC, C::OCC)))
 bwd_dq_kernel(BwdParams P, int n_qtiles) {
   constexpr int D = C::D, BN = C::BN, NB = C::NB, NE = C::NE, RB = C::RB, NP = C::NP;
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 31, hf = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 31, hf = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps per-wave branches scalar
 
   const int G = gridDim.x;
   int w = blockIdx.x;
@@ -376,8 +416,8 @@ bwd_dq_kernel(BwdParams P, int n_qtiles) {
   }
   float lse_l2 = kInf, dlt = 0.f;
   if (qrow < N) {
-    lse_l2 = P.ld[2 * ((size_t)bh * N + qrow)];
-    dlt = P.ld[2 * ((size_t)bh * N + qrow) + 1];
+    lse_l2 = P.ld[(size_t)bh * N + qrow];
+    dlt = -P.ld[(size_t)P.rows + (size_t)bh * N + qrow];
   }
   const float sl2 = P.scale_log2;
 
@@ -494,23 +534,26 @@ static hipError_t launch_pre(const BwdParams& p, long long rows, hipStream_t st)
   return hipGetLastError();
 }
 
-template <class KC, class QC>
+template <class KCA, class KCD, class QC>
 static hipError_t launch_bwd(int variant, const BwdParams& p, int B, int H, hipStream_t st) {
   const long long rows = (long long)B * H * p.N;
-  hipError_t e = launch_pre<KC::D>(p, rows, st);
+  hipError_t e = launch_pre<KCD::D>(p, rows, st);
   if (e != hipSuccess) return e;
-  const int nk = (p.N + KC::BK - 1) / KC::BK;
-  const long long gk = (long long)nk * B * H;
-  if (gk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (variant == 0) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<KC, true>), dim3((unsigned)gk), dim3(KC::NT), 0, st, p, nk);
+    const int nk = (p.N + KCA::BK - 1) / KCA::BK;
+    const long long gk = (long long)nk * B * H;
+    if (gk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<KCA, true>), dim3((unsigned)gk), dim3(KCA::NT), 0, st, p, nk);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const long long n8 = rows * KC::D / 8;
+    const long long n8 = rows * KCA::D / 8;
     hipLaunchKernelGGL(bwd_dq_convert_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, p.dq_accum,
                        reinterpret_cast<__bf16*>(p.dq), n8);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((bwd_dkdv_kernel<KC, false>), dim3((unsigned)gk), dim3(KC::NT), 0, st, p, nk);
+  const int nk = (p.N + KCD::BK - 1) / KCD::BK;
+  const long long gk = (long long)nk * B * H;
+  if (gk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<KCD, false>), dim3((unsigned)gk), dim3(KCD::NT), 0, st, p, nk);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (variant == 2) return hipSuccess;  // dK/dV only
   const int nq = (p.N + QC::BM - 1) / QC::BM;
@@ -522,11 +565,16 @@ static hipError_t launch_bwd(int variant, const BwdParams& p, int B, int H, hipS
 
 bool bwd_supported(int D) { return D == 64 || D == 128; }
 
-// Parameter table for the backward: D -> key pass (waves, query tile, waves
-// per SIMD) and dQ pass (waves, key tile, waves per SIMD).
+// Parameter table for the backward: D -> key pass with atomic dQ (waves,
+// query tile, waves per SIMD), key pass without, and the dQ pass (waves, key
+// tile, waves per SIMD). The atomic pass holds a K tile and a dS^T tile in LDS
+// on top of the stages, so it runs one workgroup per CU with larger query tiles;
+// the plain key pass at D=128 uses 32-query tiles to fit two waves per SIMD.
 hipError_t bwd_dispatch(int D, int variant, const BwdParams& p, int B, int H, hipStream_t st) {
-  if (D == 64) return launch_bwd<DkdvCfg<64, 4, 64, 2>, DqCfg<64, 4, 64, 2>>(variant, p, B, H, st);
-  if (D == 128) return launch_bwd<DkdvCfg<128, 4, 64, 1>, DqCfg<128, 4, 64, 2>>(variant, p, B, H, st);
+  if (D == 64)
+    return launch_bwd<DkdvCfg<64, 4, 64, 2>, DkdvCfg<64, 4, 64, 2>, DqCfg<64, 4, 64, 2>>(variant, p, B, H, st);
+  if (D == 128)
+    return launch_bwd<DkdvCfg<128, 4, 64, 1>, DkdvCfg<128, 4, 32, 2>, DqCfg<128, 4, 64, 2>>(variant, p, B, H, st);
   return hipErrorInvalidValue;
 }
 

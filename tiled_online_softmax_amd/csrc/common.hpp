@@ -115,11 +115,51 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const char* p) {
 // accumulator lane holds its rows, h = lane / 32), CL = false gives 8h + 4u + i.
 // Further 16-row contraction chunks add 16 * RB bytes.
 template <int RB, bool CL>
-__device__ __forceinline__ uint32_t tr16_off(int lane, int e, int u) {
+__device__ __forceinline__ constexpr uint32_t tr16_off(int lane, int e, int u) {
   const int j = lane & 15, g = lane >> 4, h = g >> 1;
   const int row = CL ? (8 * u + 4 * h + (j >> 2)) : (8 * h + 4 * u + (j >> 2));
   const int chunk = 4 * e + 2 * (g & 1) + ((j & 3) >> 1);
   return tile_off<RB>(row, chunk) + 8 * (j & 1);
+}
+
+// XOR forms of per-lane operand offsets. The swizzle only permutes 16-byte
+// chunks within a 256-byte line, so for the row sizes used here the offset of
+// operand piece p (or of column block e, slot group u) is the offset of piece 0
+// XOR a constant that is the same for every lane. A kernel can then keep one
+// base register per operand kind and fold the constant in at each read rather
+// than hold one offset register per piece. The *_ok() checks prove the identity
+// for every lane at compile time.
+//
+// Row-major operand pieces: lane (row li < 32, half hf) reads logical chunk
+// 2p + hf of row li.
+__device__ __forceinline__ constexpr uint32_t piece_xor(int p) { return (uint32_t)p << 5; }
+template <int RB, int NP>
+__device__ __forceinline__ constexpr bool piece_xor_ok() {
+  for (int li = 0; li < 32; ++li)
+    for (int hf = 0; hf < 2; ++hf)
+      for (int p = 0; p < NP; ++p)
+        if (tile_off<RB>(li, 2 * p + hf) != (tile_off<RB>(li, hf) ^ piece_xor(p))) return false;
+  return true;
+}
+// Transposed pieces read with lds_read_tr16.
+template <int RB, bool CL>
+__device__ __forceinline__ constexpr uint32_t tr16_xor(int e, int u) {
+  return tr16_off<RB, CL>(0, e, u) ^ tr16_off<RB, CL>(0, 0, 0);
+}
+template <int RB, bool CL, int NE>
+__device__ __forceinline__ constexpr bool tr16_xor_ok() {
+  for (int lane = 0; lane < 64; ++lane)
+    for (int e = 0; e < NE; ++e)
+      for (int u = 0; u < 2; ++u)
+        if (tr16_off<RB, CL>(lane, e, u) != (tr16_off<RB, CL>(lane, 0, 0) ^ tr16_xor<RB, CL>(e, u))) return false;
+  return true;
+}
+
+// Hides a value's origin from the optimiser, so expressions computed from it
+// inside a loop are not hoisted out of the loop into registers of their own.
+template <class T>
+__device__ __forceinline__ void opaque(T& x) {
+  asm volatile("" : "+v"(x));
 }
 
 // Transposing 8-byte LDS read of 8-bit elements (gfx950). Within each group

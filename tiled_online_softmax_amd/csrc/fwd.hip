@@ -61,7 +61,8 @@ fwd_kernel(FwdParams P) {
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
   constexpr int D = C::D, BN = C::BN, NB = C::NB, NE = C::NE, RB = C::RB, NP = C::NP;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps per-wave branches scalar
   const int li = lane & 31, hf = lane >> 5;
 
   // Workgroup -> (head, query tile). Consecutive workgroups go to different

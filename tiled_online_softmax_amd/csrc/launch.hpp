@@ -37,7 +37,8 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  float* ld;        // [B,H,N,2] workspace: (lse * log2(e), rowsum(dO * O)) per row
+  float* ld;        // workspace: [B*H*N] lse * log2(e), then [B*H*N] -rowsum(dO * O)
+  long long rows;   // B * H * N
   float* dq_accum;  // [B,H,N,D] float workspace (atomic variant), else nullptr
   int N;
   int causal;
