@@ -437,14 +437,10 @@ bwd_dq_kernel(BwdParams P, int n_qtiles) {
       buf_load_lds16(rv, goff[i] + base, 0, (lds_void*)(kb + C::TILE + m * 1024));
     }
   };
-  uint32_t koff[NP];
-#pragma unroll
-  for (int p = 0; p < NP; ++p) koff[p] = tile_off<RB>(li, 2 * p + hf);
-  uint32_t troff[NE][2];  // K^T operands, key order of the S^T accumulator
-#pragma unroll
-  for (int e = 0; e < NE; ++e)
-#pragma unroll
-    for (int u = 0; u < 2; ++u) troff[e][u] = tr16_off<RB, true>(lane, e, u);
+  // One base register per operand kind (see the key-tile pass).
+  static_assert(piece_xor_ok<RB, NP>() && tr16_xor_ok<RB, true, NE>(), "offset XOR form");
+  uint32_t kbase = tile_off<RB>(li, hf);
+  uint32_t tbase = tr16_off<RB, true>(lane, 0, 0);  // K^T operands, key order of the S^T accumulator
 
   f32x16 acc[NE];
 #pragma unroll
@@ -464,43 +460,82 @@ bwd_dq_kernel(BwdParams P, int n_qtiles) {
     if (more) issue(key0 + BN, nxt);
     const char* ks = cur;
     const char* vs = ks + C::TILE;
+    opaque(kbase);
+    opaque(tbase);
     if (!P.causal || key0 <= qw + 31) {
+      // S^T = K Q^T and dP^T - D = V dO^T - D, K/V pieces read one piece ahead.
       f32x16 s[NB], dp[NB];
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         s[b] = f32x16{};
-        dp[b] = f32x16{};
 #pragma unroll
-        for (int p = 0; p < NP; ++p) {
-          const i32x4 x = *reinterpret_cast<const i32x4*>(ks + koff[p] + 32 * b * RB);
-          s[b] = mfma_bf16(__builtin_bit_cast(bf16x8, x), __builtin_bit_cast(bf16x8, qf[p]), s[b]);
-          const i32x4 y = *reinterpret_cast<const i32x4*>(vs + koff[p] + 32 * b * RB);
-          dp[b] = mfma_bf16(__builtin_bit_cast(bf16x8, y), __builtin_bit_cast(bf16x8, dof[p]), dp[b]);
-        }
+        for (int v = 0; v < 16; ++v) dp[b][v] = -dlt;
       }
-      const bool need_mask = (key0 + BN > N) || (P.causal && key0 + BN - 1 > qw);
+      constexpr int LA = 1;
+      i32x4 xk[LA + 1][NB], xv[LA + 1][NB];
+      auto rd = [&](int p) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const uint32_t o = (kbase ^ piece_xor(p)) + 32 * b * RB;
+          xk[p % (LA + 1)][b] = *reinterpret_cast<const i32x4*>(ks + o);
+          xv[p % (LA + 1)][b] = *reinterpret_cast<const i32x4*>(vs + o);
+        }
+      };
+#pragma unroll
+      for (int p = 0; p < LA; ++p) rd(p);
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        if (p + LA < NP) rd(p + LA);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          s[b] = mfma_bf16(__builtin_bit_cast(bf16x8, xk[p % (LA + 1)][b]), __builtin_bit_cast(bf16x8, qf[p]), s[b]);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          dp[b] = mfma_bf16(__builtin_bit_cast(bf16x8, xv[p % (LA + 1)][b]), __builtin_bit_cast(bf16x8, dof[p]), dp[b]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float pv = fast_exp2(__builtin_fmaf(s[b][v], sl2, -lse_l2));
-          if (need_mask) {
+        for (int v = 0; v < 16; ++v) s[b][v] = fast_exp2(__builtin_fmaf(s[b][v], sl2, -lse_l2));
+      // Masked tiles (causal diagonal, ragged tail) only; the flag is wave-uniform.
+      if ((key0 + BN > N) || (P.causal && key0 + BN - 1 > qw)) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
             const int kk = key0 + 32 * b + (v >> 2) * 8 + 4 * hf + (v & 3);
-            if (kk >= N || (P.causal && kk > qrow)) pv = 0.f;
+            if (kk >= N || (P.causal && kk > qrow)) s[b][v] = 0.f;
           }
-          dp[b][v] = pv * (dp[b][v] - dlt);
+      }
+      // dS^T = P^T (dP^T - D) as bf16 pieces of 16 keys
+      bf16x8 db[BN / 16];
+#pragma unroll
+      for (int kc = 0; kc < BN / 16; ++kc)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int b = kc >> 1, v = (kc & 1) * 8 + i;
+          db[kc][i] = (__bf16)(s[b][v] * dp[b][v]);
         }
+      // dQ^T += K^T dS^T over 16-key chunks kc and 32-column blocks e; the
+      // transposed K pieces are read LB steps ahead.
+      constexpr int NS = BN / 16 * NE, LB = 2;
+      s16x4 tk[LB + 1][2];
+      auto rdt = [&](int st) {
+        const int kc = st / NE, e = st % NE;
 #pragma unroll
-      for (int kc = 0; kc < BN / 16; ++kc) {
-        bf16x8 db;
+        for (int u = 0; u < 2; ++u)
+          tk[st % (LB + 1)][u] = lds_read_tr16(ks + (tbase ^ tr16_xor<RB, true>(e, u)) + kc * 16 * RB);
+      };
 #pragma unroll
-        for (int i = 0; i < 8; ++i) db[i] = (__bf16)dp[kc >> 1][(kc & 1) * 8 + i];
+      for (int st = 0; st < LB; ++st) rdt(st);
 #pragma unroll
-        for (int e = 0; e < NE; ++e) {
-          const s16x4 x[2] = {lds_read_tr16(ks + troff[e][0] + kc * 16 * RB),
-                              lds_read_tr16(ks + troff[e][1] + kc * 16 * RB)};
-          acc[e] = mfma_bf16(__builtin_bit_cast(bf16x8, x), db, acc[e]);
-        }
+      for (int st = 0; st < NS; ++st) {
+        if (st + LB < NS) rdt(st + LB);
+        __builtin_amdgcn_sched_barrier(0);
+        acc[st % NE] = mfma_bf16(__builtin_bit_cast(bf16x8, tk[st % (LB + 1)]), db[st / NE], acc[st % NE]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (more) wait_vmem();

@@ -225,13 +225,17 @@ fwd_kernel(FwdParams P) {
           for (int v = 0; v < 16; ++v)
             if (32 * b + (v >> 2) * 8 + (v & 3) > lim) s[b][v] = -INFINITY;
       }
-      // row max: four independent max3 chains, then the partner lane
-      float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      // row max: two chains of three-way maxima (each step folds two scores into
+      // the running value, which maps to one max3), then the partner lane
+      float m2[2] = {-INFINITY, -INFINITY};
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int v = 0; v < 16; v += 2) m4[(v >> 1) & 3] = fmaxf(m4[(v >> 1) & 3], fmaxf(s[b][v], s[b][v + 1]));
-      const float mx = pair_max32(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) * sc;
+        for (int v = 0; v < 16; v += 2) {
+          float& m = m2[(v >> 3) & 1];
+          m = fmaxf(fmaxf(m, s[b][v]), s[b][v + 1]);
+        }
+      const float mx = pair_max32(fmaxf(m2[0], m2[1])) * sc;
       // ---- conditional rescale ----
       const bool grow = mx > m_ref + tau;
       if (wave_any(grow)) {
