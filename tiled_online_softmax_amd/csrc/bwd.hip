@@ -113,11 +113,9 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 31, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps per-wave branches scalar
 
-  const int G = gridDim.x;
-  int w = blockIdx.x;
-  if ((G & 7) == 0) w = (w & 7) * (G >> 3) + (w >> 3);
-  const int bh = w / n_ktiles;
-  const int kt = w % n_ktiles;  // ascending: under causal masking the first key tiles have the most work
+  // under causal masking the first key tiles see the most query tiles: rank 0 is key tile 0
+  int bh, kt;
+  wg_map(n_ktiles, P.causal, bh, kt);
   const int N = P.N;
   const int k0 = kt * C::BK;
   const int kw = k0 + 32 * wave;
@@ -390,11 +388,8 @@ bwd_dq_kernel(BwdParams P, int n_qtiles) {
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 31, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps per-wave branches scalar
 
-  const int G = gridDim.x;
-  int w = blockIdx.x;
-  if ((G & 7) == 0) w = (w & 7) * (G >> 3) + (w >> 3);
-  const int bh = w / n_qtiles;
-  int qt = w % n_qtiles;
+  int bh, qt;
+  wg_map(n_qtiles, P.causal, bh, qt);
   if (P.causal) qt = n_qtiles - 1 - qt;
   const int N = P.N;
   const int q0 = qt * C::BM;

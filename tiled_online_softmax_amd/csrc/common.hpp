@@ -183,6 +183,28 @@ __device__ __forceinline__ uint32_t tr8_off(int lane, int e) {
   return tile_off<RB>(row, 2 * e + (g & 1)) + 8 * (j & 1);
 }
 
+// Workgroup -> (head, tile rank). blockIdx values are dealt round-robin to the
+// 8 XCDs in dispatch order. Without causal masking every tile costs the same:
+// each XCD gets a contiguous run of workgroups (whole heads when the tile count
+// allows), so the K/V of a head stay in one L2. Under causal masking the tiles
+// of a head cost from one to n_tiles units, and a head-by-head order leaves
+// long workgroups for the end of the launch; there the order is rank-major
+// (rank 0, the costliest tile, of every head first), which schedules the
+// longest workgroups first, and head h stays on XCD h % 8 when the head count
+// is a multiple of 8.
+__device__ __forceinline__ void wg_map(int n_tiles, bool causal, int& bh, int& rank) {
+  const int G = gridDim.x, g = blockIdx.x;
+  if (causal) {
+    const int BH = G / n_tiles;
+    bh = g % BH;
+    rank = g / BH;
+  } else {
+    const int w = (G & 7) == 0 ? (g & 7) * (G >> 3) + (g >> 3) : g;
+    bh = w / n_tiles;
+    rank = w % n_tiles;
+  }
+}
+
 // vmcnt(0): all of this wave's vector-memory operations (incl. LDS DMA) done.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 

@@ -65,15 +65,10 @@ fwd_kernel(FwdParams P) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps per-wave branches scalar
   const int li = lane & 31, hf = lane >> 5;
 
-  // Workgroup -> (head, query tile). Consecutive workgroups go to different
-  // XCDs (round-robin), so regroup: each XCD gets a contiguous run of heads
-  // (K/V of a head stay in one L2); within a head, causal runs the longest
-  // (last) query tiles first.
-  const int G = gridDim.x;
-  int w = blockIdx.x;
-  if ((G & 7) == 0) w = (w & 7) * (G >> 3) + (w >> 3);
-  const int bh = w / P.n_qtiles;
-  int qt = w % P.n_qtiles;
+  // Workgroup -> (head, query tile); under causal masking the last query
+  // tiles carry the most key tiles, so rank 0 is the last one.
+  int bh, qt;
+  wg_map(P.n_qtiles, P.causal, bh, qt);
   if (P.causal) qt = P.n_qtiles - 1 - qt;
   const int N = P.N;
   const int q0 = qt * C::BM;
