@@ -255,15 +255,26 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
 #pragma unroll
           for (int t = 0; t < 4; ++t) s[a][4 * g + t] = fast_exp2(__builtin_fmaf(s[a][4 * g + t], sl2, -l2[t]));
         }
-      // Masked tiles (causal diagonal, ragged tail) only; the flag is wave-uniform.
-      if ((P.causal && q0 < kw + 31) || (q0 + BQ > N)) {
+      // Masked tiles only, as wave-uniform branches (opaque() on the bound keeps
+      // the compiler from flattening them into selects run on every tile).
+      // Element (a, v) is query q0 + 4h + r with r = 32a + 8(v/4) + v%4.
+      if (P.causal && q0 < kw + 31) {  // causal diagonal: keep query >= key
+        int lo = key - q0 - 4 * hf;
+        opaque(lo);
 #pragma unroll
         for (int a = 0; a < NA; ++a)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int q = q0 + 32 * a + 8 * (v >> 2) + 4 * hf + (v & 3);
-            if (q >= N || (P.causal && key > q)) s[a][v] = 0.f;
-          }
+          for (int v = 0; v < 16; ++v)
+            if (32 * a + 8 * (v >> 2) + (v & 3) < lo) s[a][v] = 0.f;
+      }
+      if (q0 + BQ > N) {  // ragged tail: keep query < N
+        int hi = N - q0 - 4 * hf;
+        opaque(hi);
+#pragma unroll
+        for (int a = 0; a < NA; ++a)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (32 * a + 8 * (v >> 2) + (v & 3) >= hi) s[a][v] = 0.f;
       }
       // dS = P (dP - D); both to bf16 pieces
 #pragma unroll
@@ -494,15 +505,18 @@ bwd_dq_kernel(BwdParams P, int n_qtiles) {
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int v = 0; v < 16; ++v) s[b][v] = fast_exp2(__builtin_fmaf(s[b][v], sl2, -lse_l2));
-      // Masked tiles (causal diagonal, ragged tail) only; the flag is wave-uniform.
+      // Masked tiles (causal diagonal, ragged tail) only, as a wave-uniform
+      // branch (see the key-tile pass). Element (b, v) is key key0 + 4h + r
+      // with r = 32b + 8(v/4) + v%4, kept iff the key is <= min(qrow, N-1)
+      // (causal) or <= N-1.
       if ((key0 + BN > N) || (P.causal && key0 + BN - 1 > qw)) {
+        int lim = (P.causal ? min(qrow, N - 1) : N - 1) - key0 - 4 * hf;
+        opaque(lim);
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int kk = key0 + 32 * b + (v >> 2) * 8 + 4 * hf + (v & 3);
-            if (kk >= N || (P.causal && kk > qrow)) s[b][v] = 0.f;
-          }
+          for (int v = 0; v < 16; ++v)
+            if (32 * b + 8 * (v >> 2) + (v & 3) > lim) s[b][v] = 0.f;
       }
       // dS^T = P^T (dP^T - D) as bf16 pieces of 16 keys
       bf16x8 db[BN / 16];

@@ -346,6 +346,278 @@ fwd_kernel(FwdParams P) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 forward, software-pipelined across key tiles.
+//
+// Same tiling, data layout and numerics as fwd_kernel; only the order of work
+// differs. Iteration j of the tile loop issues the score MFMAs of tile j+1
+// (S_{j+1} = K_{j+1} Q^T) and, between them, the VALU work that turns S_j into
+// P_j (exponentials, bf16 packing, row sums); it then issues the P.V MFMAs of
+// tile j and, between them, the masking and row max of S_{j+1} and the
+// conditional rescale. A wave's instruction stream thus alternates MFMAs with
+// independent VALU work, which the SIMD executes while the MFMAs run, rather
+// than a block of MFMAs followed by a block of softmax arithmetic.
+//
+// LDS holds two K and two V tiles; K runs one tile ahead of V:
+//   iteration j reads K_{j+1} from Kb[(j+1)%2] and V_j from Vb[j%2], and its
+//   LDS-DMA loads fill Kb[j%2] with K_{j+2} and Vb[(j+1)%2] with V_{j+1}, the
+//   buffers read by iteration j-1 (all waves passed the barrier ending it).
+// ---------------------------------------------------------------------------
+template <class C>
+__global__ void __launch_bounds__(C::NT)
+__attribute__((amdgpu_waves_per_eu(C::OCC, C::OCC)))
+fwd_pipe_kernel(FwdParams P) {
+  static_assert(C::elt == Elt::BF16, "bf16 only");
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+  constexpr int D = C::D, BN = C::BN, NB = C::NB, NE = C::NE, RB = C::RB, NP = C::NP, TILE = C::TILE;
+  constexpr int NC = BN / 16;  // 16-key chunks of a tile (P.V contraction steps)
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 31, hf = lane >> 5;
+
+  int bh, qt;
+  wg_map(P.n_qtiles, P.causal, bh, qt);
+  if (P.causal) qt = P.n_qtiles - 1 - qt;
+  const int N = P.N;
+  const int q0 = qt * C::BM;
+  const int qw = q0 + 32 * wave;
+  const int qrow = qw + li;
+
+  const size_t head_elems = (size_t)N * D;
+  const uint32_t head_bytes = (uint32_t)(head_elems * 2);
+  const auto rq = make_rsrc(reinterpret_cast<const char*>(P.q) + (size_t)bh * head_elems * 2, head_bytes);
+  const auto rk = make_rsrc(reinterpret_cast<const char*>(P.k) + (size_t)bh * head_elems * 2, head_bytes);
+  const auto rv = make_rsrc(reinterpret_cast<const char*>(P.v) + (size_t)bh * head_elems * 2, head_bytes);
+  const float sc = P.scale_log2;
+  const float tau = P.rescale_log2;
+
+  uint32_t goff[C::LPW];
+#pragma unroll
+  for (int i = 0; i < C::LPW; ++i) {
+    int row, ch;
+    tile_pos<RB>((wave * C::LPW + i) * 64 + lane, row, ch);
+    goff[i] = (uint32_t)(row * RB + ch * 16);
+  }
+  auto issue = [&](const __amdgpu_buffer_rsrc_t& r, int t, char* dst) {
+    const uint32_t base = (uint32_t)(t * BN) * RB;
+#pragma unroll
+    for (int i = 0; i < C::LPW; ++i)
+      buf_load_lds16(r, goff[i] + base, 0, (lds_void*)(dst + (wave * C::LPW + i) * 1024));
+  };
+
+  i32x4 qf[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) qf[p] = buf_load16(rq, (uint32_t)qrow * RB + 32 * p + 16 * hf);
+
+  static_assert(piece_xor_ok<RB, NP>() && tr16_xor_ok<RB, true, NE>(), "offset XOR form");
+  uint32_t kbase = tile_off<RB>(li, hf);
+  uint32_t vbase = tr16_off<RB, true>(lane, 0, 0);
+
+  f32x16 acc[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) acc[e] = f32x16{};
+  float m_ref = -INFINITY, l_part = 0.f;
+
+  const int kv_end = P.causal ? min(N, q0 + C::BM) : N;
+  const int n_tiles = (kv_end + BN - 1) / BN;
+  // key tiles holding at least one key this wave's queries may see
+  const int n_live = P.causal ? min(n_tiles, (qw + 31) / BN + 1) : n_tiles;
+
+  char* const kb0 = smem;
+  char* const kb1 = smem + TILE;
+  char* const vb0 = smem + 2 * TILE;
+  char* const vb1 = smem + 3 * TILE;
+
+  // ---- S = K Q^T for one tile, optionally interleaved with P-work ----
+  // VALU work on the previous scores comes in 2*NC half-chunks; half-chunk h
+  // (4 keys of chunk h/2 per lane) runs next to score step (h * NP) / (2 NC).
+  f32x16 sa[NB], sb[NB];  // scores of the tile being finished / being computed
+  bf16x8 pb[NC];
+  float l4[4];
+  auto half_chunk = [&](f32x16 (&s)[NB], int h, float neg_m) {
+    const int kc = h >> 1, o = (kc & 1) * 8 + (h & 1) * 4;
+    f32x16& sv = s[kc >> 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[o + i] = fast_exp2(__builtin_fmaf(sv[o + i], sc, neg_m));
+    if (h & 1) {
+      const int o8 = (kc & 1) * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pb[kc][i] = (__bf16)sv[o8 + i];
+      i32x4 pw = __builtin_bit_cast(i32x4, pb[kc]);
+      opaque(pw);  // keeps this work here (not sunk next to its use in P.V)
+      pb[kc] = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        l4[i] = dot2_bf16_sum(pw[i], l4[i]);
+        opaque(l4[i]);
+      }
+    }
+  };
+  // with_s: compute scores of tile t from kt into sn; with_p: turn sp into P.
+  auto scores_and_p = [&](const bool with_s, const bool with_p, const char* __restrict__ kt, f32x16 (&sn)[NB],
+                          f32x16 (&sp)[NB]) __attribute__((always_inline)) {
+    const float neg_m = -m_ref;
+    l4[0] = l4[1] = l4[2] = l4[3] = 0.f;
+    if (with_s) {
+      constexpr int KLA = 2;
+      i32x4 ka[KLA + 1][NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) sn[b] = f32x16{};
+#pragma unroll
+      for (int p = 0; p < KLA; ++p)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          ka[p][b] = *reinterpret_cast<const i32x4*>(kt + (kbase ^ piece_xor(p)) + 32 * b * RB);
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        if (p + KLA < NP) {
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+            ka[(p + KLA) % (KLA + 1)][b] =
+                *reinterpret_cast<const i32x4*>(kt + (kbase ^ piece_xor(p + KLA)) + 32 * b * RB);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          sn[b] = mfma_bf16(__builtin_bit_cast(bf16x8, ka[p % (KLA + 1)][b]), __builtin_bit_cast(bf16x8, qf[p]), sn[b]);
+        if (with_p) {
+#pragma unroll
+          for (int h = 0; h < 2 * NC; ++h)
+            if ((h * NP) / (2 * NC) == p) half_chunk(sp, h, neg_m);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else if (with_p) {
+#pragma unroll
+      for (int h = 0; h < 2 * NC; ++h) half_chunk(sp, h, neg_m);
+    }
+    if (with_p) l_part += (l4[0] + l4[1]) + (l4[2] + l4[3]);
+  };
+
+  // ---- mask + row max of a score tile, then the conditional rescale ----
+  // with_pv: P.V MFMAs of the previous tile run interleaved (vt = its V tile).
+  auto pv_and_max = [&](const bool with_pv, const bool with_max, const char* __restrict__ vt, int t,
+                        f32x16 (&s)[NB], bool use_max) __attribute__((always_inline)) {
+    if (with_max && use_max) {
+      const int key0 = t * BN;
+      if ((key0 + BN > N) || (P.causal && key0 + BN - 1 > qw)) {
+        int lim = (P.causal ? min(qrow, N - 1) : N - 1) - key0 - 4 * hf;
+        opaque(lim);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (32 * b + (v >> 2) * 8 + (v & 3) > lim) s[b][v] = -INFINITY;
+      }
+    }
+    float m2[2] = {-INFINITY, -INFINITY};
+    auto max_part = [&](int kc) {
+      // keys of chunk kc: s[kc/2][(kc%2)*8 .. +8]
+      const f32x16& sv = s[kc >> 1];
+      const int o = (kc & 1) * 8;
+#pragma unroll
+      for (int v = 0; v < 8; v += 2) m2[kc & 1] = fmaxf(fmaxf(m2[kc & 1], sv[o + v]), sv[o + v + 1]);
+    };
+    if (with_pv) {
+      s16x4 va[2][NE][2];
+#pragma unroll
+      for (int e = 0; e < NE; ++e)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) va[0][e][u] = lds_read_tr16(vt + (vbase ^ tr16_xor<RB, true>(e, u)));
+#pragma unroll
+      for (int kc = 0; kc < NC; ++kc) {
+        if (kc + 1 < NC) {
+#pragma unroll
+          for (int e = 0; e < NE; ++e)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+              va[(kc + 1) & 1][e][u] = lds_read_tr16(vt + (vbase ^ tr16_xor<RB, true>(e, u)) + (kc + 1) * 16 * RB);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int e = 0; e < NE; ++e) acc[e] = mfma_bf16(__builtin_bit_cast(bf16x8, va[kc & 1][e]), pb[kc], acc[e]);
+        if (with_max) max_part(kc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else if (with_max) {
+#pragma unroll
+      for (int kc = 0; kc < NC; ++kc) max_part(kc);
+    }
+    if (with_max) {
+      const float mx = pair_max32(fmaxf(m2[0], m2[1])) * sc;
+      const bool grow = mx > m_ref + tau;
+      if (use_max && wave_any(grow)) {
+        const float m_new = grow ? mx : m_ref;
+        const float alpha = fast_exp2(m_ref - m_new);
+        m_ref = m_new;
+        l_part *= alpha;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) acc[e] *= alpha;
+      }
+    }
+  };
+
+  // ---- prologue: K_0, V_0, K_1 in; S_0 and its max ----
+  issue(rk, 0, kb0);
+  issue(rv, 0, vb0);
+  if (n_tiles > 1) issue(rk, 1, kb1);
+  wait_vmem();
+  __syncthreads();
+  if (n_live > 0) {
+    scores_and_p(true, false, kb0, sa, sb);
+    pv_and_max(false, true, vb0, 0, sa, true);
+  }
+  __syncthreads();  // every wave is done with Kb[0] before K_2 overwrites it
+
+  // One iteration; sc_ holds S_j on entry, sn_ receives S_{j+1}.
+  auto iter = [&](int j, const char* __restrict__ kcur, const char* __restrict__ vcur, char* __restrict__ knxt,
+                  char* __restrict__ vnxt, f32x16 (&sc_)[NB], f32x16 (&sn_)[NB]) __attribute__((always_inline)) {
+    if (j + 1 < n_tiles) issue(rv, j + 1, vnxt);
+    if (j + 2 < n_tiles) issue(rk, j + 2, knxt);
+    opaque(kbase);
+    opaque(vbase);
+    if (j < n_live) {
+      // the last live tile also computes (and discards) scores for the next tile
+      scores_and_p(true, true, kcur, sn_, sc_);
+      pv_and_max(true, true, vcur, j + 1, sn_, j + 1 < n_live);
+    }
+    if (j + 1 < n_tiles) wait_vmem();
+    __syncthreads();
+  };
+  for (int j = 0; j < n_tiles; j += 2) {
+    iter(j, kb1, vb0, kb0, vb1, sa, sb);
+    if (j + 1 < n_tiles) iter(j + 1, kb0, vb1, kb1, vb0, sb, sa);
+  }
+
+  // ---- epilogue: O = acc / l, lse = ln(sum exp(s)) ----
+  const float l_tot = pair_sum32(l_part);
+  const float inv = 1.f / l_tot;
+  if (qrow < N) {
+    const size_t row_base = ((size_t)bh * N + qrow) * D;
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * e + 8 * g + 4 * hf;
+        bf16x4 o4 = {(__bf16)(acc[e][4 * g] * inv), (__bf16)(acc[e][4 * g + 1] * inv),
+                     (__bf16)(acc[e][4 * g + 2] * inv), (__bf16)(acc[e][4 * g + 3] * inv)};
+        *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(P.o) + row_base + d) = o4;
+      }
+    if (hf == 0) P.lse[(size_t)bh * N + qrow] = (m_ref + __builtin_log2f(l_tot)) * kLn2;
+  }
+}
+
+template <class C>
+static hipError_t launch_fwd_pipe(const FwdParams& p0, int B, int H, hipStream_t st) {
+  FwdParams p = p0;
+  p.n_qtiles = (p.N + C::BM - 1) / C::BM;
+  const long long grid = (long long)p.n_qtiles * B * H;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(fwd_pipe_kernel<C>, dim3((unsigned)grid), dim3(C::NT), 0, st, p);
+  return hipGetLastError();
+}
+
 template <class C>
 static hipError_t launch_fwd_direct(const FwdParams& p0, int B, int H, hipStream_t st) {
   FwdParams p = p0;
@@ -367,9 +639,9 @@ hipError_t fwd_dispatch(Elt e, int D, const FwdParams& p, int B, int H, hipStrea
       if (D == 256) return launch_fwd_direct<FwdDCfg<Elt::F32, 256, 32, 4, 1>>(p, B, H, st);
       break;
     case Elt::BF16:
-      if (D == 64) return launch_fwd_direct<FwdDCfg<Elt::BF16, 64, 64, 4, 2>>(p, B, H, st);
-      if (D == 128) return launch_fwd_direct<FwdDCfg<Elt::BF16, 128, 64, 4, 2>>(p, B, H, st);
-      if (D == 256) return launch_fwd_direct<FwdDCfg<Elt::BF16, 256, 64, 4, 1>>(p, B, H, st);
+      if (D == 64) return launch_fwd_pipe<FwdDCfg<Elt::BF16, 64, 64, 4, 2>>(p, B, H, st);
+      if (D == 128) return launch_fwd_pipe<FwdDCfg<Elt::BF16, 128, 64, 4, 2>>(p, B, H, st);
+      if (D == 256) return launch_fwd_pipe<FwdDCfg<Elt::BF16, 256, 64, 4, 1>>(p, B, H, st);
       break;
     case Elt::FP8:
       if (D == 64) return launch_fwd_direct<FwdDCfg<Elt::FP8, 64, 64, 4, 2>>(p, B, H, st);
