@@ -142,36 +142,39 @@ def breakdown():
     res = {}
     for name, w in inputs.WORKLOADS.items():
         t0 = time.time()
-        x = device_inputs(w, with_grad=(w.passes == "bwd"))
+        x = device_inputs(w, with_grad=(w.passes != "fwd"))
+        legs = []  # (label, pass, fn, flops, peak, iters)
         if w.dtype == "fp8":
             qc, qd = fa.quantize_fp8(x["q"])
             kc, kd = fa.quantize_fp8(x["k"])
             vc, vd = fa.quantize_fp8(x["v"])
             del x
             fn = lambda: fa.fwd_fp8(qc, kc, vc, causal=w.causal, q_descale=qd, k_descale=kd, v_descale=vd)
-            flops, peak, iters = w.fwd_flops(), PEAK_TFLOPS["fp8"], 10
-        elif w.passes == "fwd":
+            legs.append((name, "fwd", fn, w.fwd_flops(), PEAK_TFLOPS["fp8"], 10))
+        if w.passes in ("fwd", "fwd+bwd") and w.dtype != "fp8":
             fn = lambda: fa.fwd(x["q"], x["k"], x["v"], causal=w.causal)
-            flops = w.fwd_flops()
             peak = PEAK_TFLOPS["f32" if w.dtype == "f32" else "bf16"]
-            iters = 200 if w.N <= 2048 else 30
-        else:
+            legs.append((name if w.passes == "fwd" else name + ":fwd", "fwd", fn, w.fwd_flops(), peak,
+                         200 if w.N <= 2048 else 30))
+        if w.passes in ("bwd", "fwd+bwd"):
             o, lse = fa.fwd(x["q"], x["k"], x["v"], causal=w.causal)
             ws = torch.empty(fa.bwd_workspace_size(w.B, w.H, w.N, w.D, fa.FA_BWD_DETERMINISTIC), dtype=torch.uint8,
                              device="cuda:0")
             fn = lambda: fa.bwd(x["q"], x["k"], x["v"], o, x["do"], lse, causal=w.causal,
                                 variant=fa.FA_BWD_DETERMINISTIC, workspace=ws)
-            flops, peak, iters = w.bwd_flops(), PEAK_TFLOPS["bf16"], 50
-        try:
-            ms = time_fn(fn, iters)
-        except Exception as e:  # report, do not hide
-            res[name] = {"error": str(e)}
-            continue
-        tf = flops / (ms * 1e-3) / 1e12
-        res[name] = {"pass": w.passes, "dtype": w.dtype, "ms": round(ms, 4), "tflops": round(tf, 2),
-                     "pct_of_peak": round(100 * tf / peak, 2), "peak_tflops": peak}
-        log(f"[breakdown] {name}: {ms:.4f} ms  {tf:.1f} TFLOP/s  ({100 * tf / peak:.1f}% of {peak})"
-            f"  [{time.time() - t0:.1f}s]")
+            legs.append((name if w.passes == "bwd" else name + ":bwd", "bwd", fn, w.bwd_flops(), PEAK_TFLOPS["bf16"],
+                         50))
+        for label, pss, fn, flops, peak, iters in legs:
+            try:
+                ms = time_fn(fn, iters)
+            except Exception as e:  # report, do not hide
+                res[label] = {"error": str(e)}
+                continue
+            tf = flops / (ms * 1e-3) / 1e12
+            res[label] = {"pass": pss, "dtype": w.dtype, "ms": round(ms, 4), "tflops": round(tf, 2),
+                          "pct_of_peak": round(100 * tf / peak, 2), "peak_tflops": peak}
+            log(f"[breakdown] {label}: {ms:.4f} ms  {tf:.1f} TFLOP/s  ({100 * tf / peak:.1f}% of {peak})"
+                f"  [{time.time() - t0:.1f}s]")
         torch.cuda.empty_cache()
     return res
 

@@ -78,6 +78,22 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            void* stream);
 
 /*
+ * Grouped-query forward: K and V have Hkv heads, each shared by H / Hkv
+ * consecutive query heads -- query head h (0 <= h < H) attends with K/V head
+ * h / (H / Hkv) of the same batch entry. Hkv = H is fa_fwd; Hkv = 1 is
+ * multi-query attention. (Grouped-query attention is the variant the
+ * "FlashAttention" entity trail page, section "Corpus findings", reports
+ * attention kernels being carried over to, AVO entry.)
+ *   q, o   : [B, H, N, D];  k, v : [B, Hkv, N, D];  lse : [B, H, N].
+ *   dtype  : FA_F32 or FA_BF16 (D as for fa_fwd), or FA_FP8_E4M3 with unit
+ *            scales. FA_ERR_INVALID_ARG if Hkv < 1 or Hkv does not divide H.
+ * Other arguments, numerics and errors as for fa_fwd.
+ */
+int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int Hkv, int N, int D, int causal, float scale,
+               int dtype, void* stream);
+
+/*
  * fa_fwd with an explicit conditional-rescale threshold `rescale_log2`
  * (>= 0, in base-2 units of the score): a row's reference max is moved --
  * and its accumulator rescaled -- only when a new tile's max exceeds it by
@@ -156,10 +172,26 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            int variant, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Grouped-query backward (the gradients of fa_fwd_gqa): K/V head j's dK and
+ * dV are the sums of the contributions of its H / Hkv query heads.
+ *   q, o, dO, dq : [B, H, N, D];  k, v, dk, dv : [B, Hkv, N, D];
+ *   lse          : [B, H, N];  workspace: fa_bwd_workspace_size(B, H, N, D,
+ *                  dtype, variant) bytes (H = query heads).
+ * FA_ERR_INVALID_ARG if Hkv < 1 or Hkv does not divide H; FA_ERR_UNSUPPORTED
+ * if the H / Hkv query heads of a group span 2^32 bytes or more. Other
+ * arguments, variants and errors as for fa_bwd.
+ */
+int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
+               const void* dO, const float* lse, void* dq, void* dk, void* dv,
+               int B, int H, int Hkv, int N, int D, int causal, float scale,
+               int dtype, int variant, void* workspace, size_t workspace_bytes,
+               void* stream);
+
+/*
  * dK and dV only: the preprocess and the key-tile pass of fa_bwd, without any
  * dQ work, for callers that need no gradient with respect to Q. Arguments as
  * for fa_bwd (dq is not taken); the workspace is the FA_BWD_DETERMINISTIC
- * size. The results are bitwise those of fa_bwd.
+ * size. The results are bitwise those of fa_bwd with FA_BWD_DETERMINISTIC.
  */
 int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* o,
                 const void* dO, const float* lse, void* dk, void* dv,

@@ -2,6 +2,10 @@
 
 Conventions (the pages fix none of them; these are the plainest readings):
   * tensors are contiguous [B, H, N, D]; queries and keys have the same length N;
+  * grouped-query attention (named on the page "FlashAttention" entity trail,
+    section "Corpus findings", AVO entry): K and V may have Hkv heads with Hkv
+    dividing H; query head h then uses K/V head h // (H // Hkv), i.e. each run
+    of H // Hkv consecutive query heads shares one K/V head;
   * scores are s_ij = scale * <q_i, k_j>;
   * causal keeps key j only when j <= i (with equal query and key lengths the
     top-left and bottom-right alignments coincide, and no row is empty);
@@ -30,6 +34,13 @@ def _row_blocks(n_rows, n_cols):
         yield r0, min(n_rows, r0 + rows)
 
 
+def _group(h_q, h_kv):
+    """Query heads per K/V head; H_kv must divide H_q."""
+    if h_kv < 1 or h_q % h_kv:
+        raise ValueError(f"K/V heads ({h_kv}) must divide query heads ({h_q})")
+    return h_q // h_kv
+
+
 def scores(q, k, scale, causal, rows=None):
     """S[i, j] = scale * q_i . k_j for one head, masked entries set to -inf.
 
@@ -56,7 +67,8 @@ def forward(q, k, v, causal, scale, rows=None):
     """Attention forward for all heads.
 
     Args:
-      q, k, v: [B, H, N, D] arrays (any float dtype; widened to float64).
+      q: [B, H, N, D]; k, v: [B, Hkv, N, D] with Hkv dividing H (any float
+        dtype; widened to float64).
       causal: keep key j only for j <= i.
       scale: the factor on q.k.
       rows: optional sorted 1-D array of query indices; when given, only those
@@ -68,17 +80,19 @@ def forward(q, k, v, causal, scale, rows=None):
     k = _as_f64(k)
     v = _as_f64(v)
     B, H, N, D = q.shape
+    G = _group(H, k.shape[1])
     sel = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
     M = sel.shape[0]
     o = np.empty((B, H, M, v.shape[-1]))
     lse = np.empty((B, H, M))
     for b in range(B):
         for h in range(H):
+            kh = h // G
             for r0, r1 in _row_blocks(M, k.shape[2]):
                 rr = sel[r0:r1]
-                s = scores(q[b, h, rr], k[b, h], scale, causal, rows=rr)
+                s = scores(q[b, h, rr], k[b, kh], scale, causal, rows=rr)
                 p, lse_blk = softmax_rows(s)
-                o[b, h, r0:r1] = p @ v[b, h]
+                o[b, h, r0:r1] = p @ v[b, kh]
                 lse[b, h, r0:r1] = lse_blk
     return o, lse
 
@@ -92,23 +106,28 @@ def backward(q, k, v, do, causal, scale):
       dP = dO V^T
       dS_i = P_i * (dP_i - <P_i, dP_i>)      (row-wise softmax Jacobian)
       dQ = scale dS K,   dK = scale dS^T Q
-    Returns (dQ, dK, dV), each [B, H, N, D] float64.
+    With grouped K/V heads (k, v of shape [B, Hkv, N, D]) a K/V head's dK and
+    dV are sums over the query heads that use it, as the chain rule gives for
+    a shared input.
+    Returns (dQ, dK, dV): dQ [B, H, N, D], dK and dV shaped like k and v, float64.
     """
     q = _as_f64(q)
     k = _as_f64(k)
     v = _as_f64(v)
     do = _as_f64(do)
     dq = np.empty_like(q)
-    dk = np.empty_like(k)
-    dv = np.empty_like(v)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
     B, H, N, D = q.shape
+    G = _group(H, k.shape[1])
     for b in range(B):
         for h in range(H):
-            s = scores(q[b, h], k[b, h], scale, causal)
+            kh = h // G
+            s = scores(q[b, h], k[b, kh], scale, causal)
             p, _ = softmax_rows(s)
-            dv[b, h] = p.T @ do[b, h]
-            dp = do[b, h] @ v[b, h].T
+            dv[b, kh] += p.T @ do[b, h]
+            dp = do[b, h] @ v[b, kh].T
             ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
-            dq[b, h] = scale * (ds @ k[b, h])
-            dk[b, h] = scale * (ds.T @ q[b, h])
+            dq[b, h] = scale * (ds @ k[b, kh])
+            dk[b, kh] += scale * (ds.T @ q[b, h])
     return dq, dk, dv

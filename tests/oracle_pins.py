@@ -18,7 +18,11 @@ own code:
     plain formula (library routines);
   * central finite differences of the forward for the backward;
   * exact backward identities: sum_j dK_j = 0, sum_j dV_j = sum_i dO_i, and
-    dQ = dK = 0 when all value rows are equal.
+    dQ = dK = 0 when all value rows are equal;
+  * grouped K/V heads: torch's scaled_dot_product_attention with enable_gqa
+    and its autograd, and the identity that a group's shared K/V head gives
+    the same outputs as every query head holding its own copy (whose dK and dV
+    then add up to the shared head's).
 """
 from __future__ import annotations
 
@@ -222,6 +226,46 @@ def pin_brute_force(fwd, bwd, brute, tol=1e-12):
             bg = brute.backward(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), do[0, 0].tolist(), causal, scale)
             for got, ref in zip(g, bg):
                 np.testing.assert_allclose(got[0, 0], np.array(ref), atol=tol)
+
+
+def pin_torch_gqa(fwd, bwd, tol=1e-11):
+    """torch CPU float64 scaled_dot_product_attention(enable_gqa=True) and its autograd (library routines)."""
+    import torch
+
+    for (B, H, Hkv, N, D, causal, seed) in [(2, 6, 2, 19, 8, False, 60), (1, 4, 1, 23, 16, True, 61),
+                                             (1, 8, 4, 9, 8, True, 62)]:
+        q, do = _rand((B, H, N, D), seed), _rand((B, H, N, D), seed + 3)
+        k, v = _rand((B, Hkv, N, D), seed + 1), _rand((B, Hkv, N, D), seed + 2)
+        scale = 1.0 / math.sqrt(D) * 0.9
+        o, lse = fwd(q, k, v, causal, scale)
+        tq, tk, tv = (torch.from_numpy(x).requires_grad_() for x in (q, k, v))
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale,
+                                                               enable_gqa=True)
+        np.testing.assert_allclose(o, ref.detach().numpy(), atol=tol)
+        ref.backward(torch.from_numpy(do))
+        dq, dk, dv = bwd(q, k, v, do, causal, scale)
+        assert dk.shape == k.shape and dv.shape == v.shape
+        for mine, theirs in ((dq, tq), (dk, tk), (dv, tv)):
+            np.testing.assert_allclose(mine, theirs.grad.numpy(), atol=tol)
+
+
+def pin_gqa_matches_copied_heads(fwd, bwd, tol=1e-12):
+    """Sharing a K/V head across a group equals giving each query head its own copy; shared grads are sums."""
+    B, H, Hkv, N, D = 2, 6, 3, 17, 8
+    G = H // Hkv
+    for causal in (False, True):
+        q, do = _rand((B, H, N, D), 70), _rand((B, H, N, D), 73)
+        k, v = _rand((B, Hkv, N, D), 71), _rand((B, Hkv, N, D), 72)
+        kr, vr = np.repeat(k, G, axis=1), np.repeat(v, G, axis=1)  # query head h gets copy of K/V head h // G
+        o, lse = fwd(q, k, v, causal, 0.4)
+        o_r, lse_r = fwd(q, kr, vr, causal, 0.4)
+        np.testing.assert_allclose(o, o_r, atol=tol)
+        np.testing.assert_allclose(lse, lse_r, atol=tol)
+        dq, dk, dv = bwd(q, k, v, do, causal, 0.4)
+        dq_r, dk_r, dv_r = bwd(q, kr, vr, do, causal, 0.4)
+        np.testing.assert_allclose(dq, dq_r, atol=tol)
+        np.testing.assert_allclose(dk, dk_r.reshape(B, Hkv, G, N, D).sum(axis=2), atol=tol)
+        np.testing.assert_allclose(dv, dv_r.reshape(B, Hkv, G, N, D).sum(axis=2), atol=tol)
 
 
 FORWARD_PINS = [pin_zero_query, pin_constant_scores, pin_ones_value, pin_permutation, pin_key_shift,

@@ -148,3 +148,37 @@ def test_bwd_dkdv_validation():
     assert L.fa_bwd_dkdv(*args, fa.FA_BF16, P, 8, None) == fa.FA_ERR_WORKSPACE
     bad = [P] * 7 + [None] + [1, 1, 16, 64, 0, 0.125]
     assert L.fa_bwd_dkdv(*bad, fa.FA_BF16, P, 1 << 20, None) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("H,Hkv,status,msg", [
+    (8, 3, fa.FA_ERR_INVALID_ARG, "divide"),
+    (8, 0, fa.FA_ERR_INVALID_ARG, "divide"),
+    (4, 8, fa.FA_ERR_INVALID_ARG, "divide"),
+    (8, -2, fa.FA_ERR_INVALID_ARG, "divide"),
+])
+def test_fwd_gqa_head_validation(H, Hkv, status, msg):
+    L = fa.lib()
+    assert L.fa_fwd_gqa(P, P, P, P, P, 1, H, Hkv, 16, 64, 0, 0.1, fa.FA_BF16, None) == status
+    assert msg in fa.last_error()
+
+
+def test_fwd_gqa_common_validation():
+    L = fa.lib()
+    assert L.fa_fwd_gqa(None, P, P, P, P, 1, 8, 2, 16, 64, 0, 0.1, fa.FA_BF16, None) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_fwd_gqa(P, P, P, P, P, 1, 8, 2, 16, 96, 0, 0.1, fa.FA_BF16, None) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_bwd_gqa_validation():
+    L = fa.lib()
+    ws = fa.bwd_workspace_size(1, 8, 16, 64, fa.FA_BWD_DETERMINISTIC)
+
+    def call(H, Hkv, N=16, D=64, variant=fa.FA_BWD_DETERMINISTIC, wsb=ws):
+        return L.fa_bwd_gqa(P, P, P, P, P, P, P, P, P, 1, H, Hkv, N, D, 0, 0.1, fa.FA_BF16, variant, P, wsb, None)
+
+    assert call(8, 3) == fa.FA_ERR_INVALID_ARG and "divide" in fa.last_error()
+    assert call(8, 0) == fa.FA_ERR_INVALID_ARG
+    assert call(8, 2, variant=2) == fa.FA_ERR_INVALID_ARG and "variant" in fa.last_error()
+    assert call(8, 2, wsb=ws - 1) == fa.FA_ERR_WORKSPACE
+    # 64 query heads of 2^20 x 64 bf16 (2^27 bytes each) share one K/V head: the group spans 2^33 bytes
+    big = fa.bwd_workspace_size(1, 64, 1 << 20, 64, fa.FA_BWD_DETERMINISTIC)
+    assert call(64, 1, N=1 << 20, wsb=big) == fa.FA_ERR_UNSUPPORTED and "2^32" in fa.last_error()

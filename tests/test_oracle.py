@@ -27,6 +27,20 @@ def test_backward_identities():
     pins.pin_backward_identities(attention.backward)
 
 
+def test_torch_gqa():
+    pins.pin_torch_gqa(attention.forward, attention.backward)
+
+
+def test_gqa_matches_copied_heads():
+    pins.pin_gqa_matches_copied_heads(attention.forward, attention.backward)
+
+
+def test_gqa_rejects_bad_groups():
+    q = np.zeros((1, 4, 3, 2))
+    with pytest.raises(ValueError):
+        attention.forward(q, np.zeros((1, 3, 3, 2)), np.zeros((1, 3, 3, 2)), False, 1.0)
+
+
 def test_brute_force():
     pins.pin_brute_force(attention.forward, attention.backward, brute)
 

@@ -114,3 +114,62 @@ def test_backward_mutant_is_caught(name):
 
 def test_unmutated_backward_passes_every_pin():
     assert _all_backward_pins(attention.backward) == 0
+
+
+def _gqa_factory(interleaved=False, overwrite=False):
+    """A grouped-query forward/backward pair with one planted mistake."""
+    def kv_index(h, G, Hkv):
+        return h % Hkv if interleaved else h // G
+
+    def fwd(q, k, v, causal, scale, rows=None):
+        q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+        B, H, N, D = q.shape
+        G = H // k.shape[1]
+        o = np.empty((B, H, N, v.shape[-1]))
+        lse = np.empty((B, H, N))
+        for b in range(B):
+            for h in range(H):
+                kh = kv_index(h, G, k.shape[1])
+                s = attention.scores(q[b, h], k[b, kh], scale, causal)
+                p, lse[b, h] = attention.softmax_rows(s)
+                o[b, h] = p @ v[b, kh]
+        return o, lse
+
+    def bwd(q, k, v, do, causal, scale):
+        q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+        B, H, N, D = q.shape
+        G = H // k.shape[1]
+        dq, dk, dv = np.empty_like(q), np.zeros_like(k), np.zeros_like(v)
+        for b in range(B):
+            for h in range(H):
+                kh = kv_index(h, G, k.shape[1])
+                p, _ = attention.softmax_rows(attention.scores(q[b, h], k[b, kh], scale, causal))
+                dp = do[b, h] @ v[b, kh].T
+                ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+                dq[b, h] = scale * (ds @ k[b, kh])
+                if overwrite:
+                    dv[b, kh] = p.T @ do[b, h]
+                    dk[b, kh] = scale * (ds.T @ q[b, h])
+                else:
+                    dv[b, kh] += p.T @ do[b, h]
+                    dk[b, kh] += scale * (ds.T @ q[b, h])
+        return dq, dk, dv
+    return fwd, bwd
+
+
+@pytest.mark.parametrize("mutant", ["interleaved_heads", "group_grads_overwritten"])
+def test_gqa_mutants_fail_a_pin(mutant):
+    fwd, bwd = _gqa_factory(interleaved=mutant == "interleaved_heads", overwrite=mutant == "group_grads_overwritten")
+    failures = 0
+    for pin in (pins.pin_torch_gqa, pins.pin_gqa_matches_copied_heads):
+        try:
+            pin(fwd, bwd)
+        except AssertionError:
+            failures += 1
+    assert failures >= 1
+
+
+def test_unmutated_gqa_factory_passes():
+    fwd, bwd = _gqa_factory()
+    pins.pin_torch_gqa(fwd, bwd)
+    pins.pin_gqa_matches_copied_heads(fwd, bwd)

@@ -113,24 +113,34 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 31, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps per-wave branches scalar
 
-  // under causal masking the first key tiles see the most query tiles: rank 0 is key tile 0
+  // Workgroup -> (K/V head, key tile); under causal masking the first key
+  // tiles see the most query tiles: rank 0 is key tile 0. The K/V head's
+  // `group` query heads are consecutive ([qbh0, qbh0 + group)), so their Q, dO
+  // and per-row values form one contiguous range of group*N rows: the pass
+  // walks the query tiles of every head of the group, which sums their dK and
+  // dV contributions in the accumulators.
   int bh, kt;
   wg_map(n_ktiles, P.causal, bh, kt);
   const int N = P.N;
+  const int group = P.group;
+  const int hkv = P.hq / group;
+  const int qbh0 = (bh / hkv) * P.hq + (bh % hkv) * group;
   const int k0 = kt * C::BK;
   const int kw = k0 + 32 * wave;
   const int key = kw + li;
 
-  const size_t head = (size_t)bh * N * D;
+  const size_t head = (size_t)bh * N * D;        // K/V head
+  const size_t qhead = (size_t)qbh0 * N * D;     // first query head of the group
   const uint32_t head_bytes = (uint32_t)((size_t)N * D * 2);
-  const auto rq = make_rsrc(reinterpret_cast<const __bf16*>(P.q) + head, head_bytes);
+  const uint32_t group_bytes = (uint32_t)((size_t)group * N * D * 2);
+  const auto rq = make_rsrc(reinterpret_cast<const __bf16*>(P.q) + qhead, group_bytes);
   const auto rk = make_rsrc(reinterpret_cast<const __bf16*>(P.k) + head, head_bytes);
   const auto rv = make_rsrc(reinterpret_cast<const __bf16*>(P.v) + head, head_bytes);
-  const auto rdo = make_rsrc(reinterpret_cast<const __bf16*>(P.dO) + head, head_bytes);
-  // lse*log2e rows of this head, and the -D rows `rows` floats further on
+  const auto rdo = make_rsrc(reinterpret_cast<const __bf16*>(P.dO) + qhead, group_bytes);
+  // lse*log2e rows of the group's query heads, and their -D rows `rows` floats further on
   const size_t rows = (size_t)P.rows;
   const auto rld = make_rsrc(P.ld, (uint32_t)(rows * 8));
-  const uint32_t ld_l2 = (uint32_t)((size_t)bh * N * 4), ld_nd = (uint32_t)((rows + (size_t)bh * N) * 4);
+  const uint32_t ld_l2 = (uint32_t)((size_t)qbh0 * N * 4), ld_nd = (uint32_t)((rows + (size_t)qbh0 * N) * 4);
 
   // K^T and V^T pieces (B operands of S = Q K^T and dP = dO V^T).
   i32x4 kf[NP], vf[NP];
@@ -147,8 +157,9 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
     tile_pos<RB>((wave * C::LPW + i) * 64 + lane, row, ch);
     goff[i] = (uint32_t)(row * RB + ch * 16);
   }
-  auto issue = [&](int q0, char* st) {
-    const uint32_t base = (uint32_t)q0 * RB;
+  // row0: first row of the tile within the group's rows (g * N + q0 for head g)
+  auto issue = [&](int row0, char* st) {
+    const uint32_t base = (uint32_t)row0 * RB;
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i) {
       const int m = wave * C::LPW + i;
@@ -158,7 +169,7 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
     // lanes 0..BQ/4-1 bring lse*log2e of the tile's rows, the next BQ/4 lanes their -D
     if (wave == 0 && lane < BQ / 2) {
       const int half = lane >= BQ / 4, j = lane - half * (BQ / 4);
-      buf_load_lds16(rld, (half ? ld_nd : ld_l2) + (uint32_t)(q0 * 4 + j * 16), 0, (lds_void*)(st + C::OFF_LD));
+      buf_load_lds16(rld, (half ? ld_nd : ld_l2) + (uint32_t)(row0 * 4 + j * 16), 0, (lds_void*)(st + C::OFF_LD));
     }
   };
 
@@ -192,6 +203,15 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
   const int nq = (N + BQ - 1) / BQ;
   const float sl2 = P.scale_log2;
 
+  // Query tiles visited, head by head of the group: (hg, it) runs over
+  // [0, group) x [qt0, nq); (nhg, nit) is the tile after it.
+  int hg = 0, it = qt0;
+  auto advance = [&](int& g, int& t) {
+    if (++t == nq) {
+      t = qt0;
+      ++g;
+    }
+  };
   issue(qt0 * BQ, smem);
   wait_vmem();
   __syncthreads();
@@ -200,11 +220,14 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
   // restrict qualifiers (also on the dS^T and K tiles) tell the compiler these
   // regions are disjoint, so it does not wait for the prefetch before reading
   // them. The prefetch is waited for explicitly at the end of the tile.
-  auto tile = [&](int it, const char* __restrict__ cur, char* __restrict__ nxt, char* __restrict__ dsb,
+  auto tile = [&](const char* __restrict__ cur, char* __restrict__ nxt, char* __restrict__ dsb,
                   const char* __restrict__ ktb) {
     const int q0 = it * BQ;
-    const bool more = it + 1 < nq;
-    if (more) issue(q0 + BQ, nxt);
+    const int qh = hg;  // this tile's query head within the group
+    int nhg = hg, nit = it;
+    advance(nhg, nit);
+    const bool more = nhg < group;
+    if (more) issue(nhg * N + nit * BQ, nxt);
     const char* qs = cur;
     const char* dos = qs + C::OFF_DO;
     const float* lds_ld = reinterpret_cast<const float*>(qs + C::OFF_LD);
@@ -336,7 +359,7 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
                               lds_read_tr16(ktb + tr16_off<RB, false>(lane, e, 1) + kc * 16 * RB)};
           c = mfma_bf16(__builtin_bit_cast(bf16x8, x), __builtin_bit_cast(bf16x8, y), c);
         }
-        float* dst = P.dq_accum + ((size_t)bh * N) * D + 32 * e + li;
+        float* dst = P.dq_accum + ((size_t)(qbh0 + qh) * N) * D + 32 * e + li;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int q = q0 + 32 * a + (v >> 2) * 8 + 4 * hf + (v & 3);
@@ -347,10 +370,12 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
 
     if (more) wait_vmem();
     __syncthreads();
+    hg = nhg;
+    it = nit;
   };
-  for (int it = qt0; it < nq; it += 2) {
-    tile(it, smem, smem + C::STAGE, ds_lds, kt_lds);
-    if (it + 1 < nq) tile(it + 1, smem + C::STAGE, smem, ds_lds, kt_lds);
+  while (hg < group) {
+    tile(smem, smem + C::STAGE, ds_lds, kt_lds);
+    if (hg < group) tile(smem + C::STAGE, smem, ds_lds, kt_lds);
   }
 
   if (key < N) {
@@ -408,10 +433,11 @@ bwd_dq_kernel(BwdParams P, int n_qtiles) {
   const int qrow = qw + li;
 
   const size_t head = (size_t)bh * N * D;
+  const size_t kvhead = (size_t)kv_head(bh, P.hq, P.group) * N * D;
   const uint32_t head_bytes = (uint32_t)((size_t)N * D * 2);
   const auto rq = make_rsrc(reinterpret_cast<const __bf16*>(P.q) + head, head_bytes);
-  const auto rk = make_rsrc(reinterpret_cast<const __bf16*>(P.k) + head, head_bytes);
-  const auto rv = make_rsrc(reinterpret_cast<const __bf16*>(P.v) + head, head_bytes);
+  const auto rk = make_rsrc(reinterpret_cast<const __bf16*>(P.k) + kvhead, head_bytes);
+  const auto rv = make_rsrc(reinterpret_cast<const __bf16*>(P.v) + kvhead, head_bytes);
   const auto rdo = make_rsrc(reinterpret_cast<const __bf16*>(P.dO) + head, head_bytes);
 
   i32x4 qf[NP], dof[NP];
@@ -581,11 +607,12 @@ static hipError_t launch_pre(const BwdParams& p, long long rows, hipStream_t st)
 template <class KCA, class KCD, class QC>
 static hipError_t launch_bwd(int variant, const BwdParams& p, int B, int H, hipStream_t st) {
   const long long rows = (long long)B * H * p.N;
+  const int HKV = H / p.group;  // the key-tile passes run over K/V heads
   hipError_t e = launch_pre<KCD::D>(p, rows, st);
   if (e != hipSuccess) return e;
   if (variant == 0) {
     const int nk = (p.N + KCA::BK - 1) / KCA::BK;
-    const long long gk = (long long)nk * B * H;
+    const long long gk = (long long)nk * B * HKV;
     if (gk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((bwd_dkdv_kernel<KCA, true>), dim3((unsigned)gk), dim3(KCA::NT), 0, st, p, nk);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -595,7 +622,7 @@ static hipError_t launch_bwd(int variant, const BwdParams& p, int B, int H, hipS
     return hipGetLastError();
   }
   const int nk = (p.N + KCD::BK - 1) / KCD::BK;
-  const long long gk = (long long)nk * B * H;
+  const long long gk = (long long)nk * B * HKV;
   if (gk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((bwd_dkdv_kernel<KCD, false>), dim3((unsigned)gk), dim3(KCD::NT), 0, st, p, nk);
   if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -190,19 +190,28 @@ __device__ __forceinline__ uint32_t tr8_off(int lane, int e) {
 // of a head cost from one to n_tiles units, and a head-by-head order leaves
 // long workgroups for the end of the launch; there the order is rank-major
 // (rank 0, the costliest tile, of every head first), which schedules the
-// longest workgroups first, and head h stays on XCD h % 8 when the head count
-// is a multiple of 8.
+// longest workgroups first. When the head count is a multiple of 8, XCD x then
+// gets the contiguous heads [x*BH/8, (x+1)*BH/8), so neighbouring query heads
+// that share K/V heads share an L2.
 __device__ __forceinline__ void wg_map(int n_tiles, bool causal, int& bh, int& rank) {
   const int G = gridDim.x, g = blockIdx.x;
   if (causal) {
     const int BH = G / n_tiles;
-    bh = g % BH;
+    const int i = g % BH;
+    bh = (BH & 7) == 0 ? (i & 7) * (BH >> 3) + (i >> 3) : i;
     rank = g / BH;
   } else {
     const int w = (G & 7) == 0 ? (g & 7) * (G >> 3) + (g >> 3) : g;
     bh = w / n_tiles;
     rank = w % n_tiles;
   }
+}
+
+// K/V head of query head bh (over B*hq heads) when `group` query heads share
+// one K/V head: batch entry bh / hq, K/V head (bh % hq) / group of hq / group.
+__device__ __forceinline__ int kv_head(int bh, int hq, int group) {
+  if (group == 1) return bh;
+  return (bh / hq) * (hq / group) + (bh % hq) / group;
 }
 
 // vmcnt(0): all of this wave's vector-memory operations (incl. LDS DMA) done.

@@ -78,8 +78,9 @@ fwd_kernel(FwdParams P) {
   const size_t head_elems = (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)(head_elems * C::ESZ);
   const char* qh = reinterpret_cast<const char*>(P.q) + (size_t)bh * head_elems * C::ESZ;
-  const char* kh = reinterpret_cast<const char*>(P.k) + (size_t)bh * head_elems * C::ESZ;
-  const char* vh = reinterpret_cast<const char*>(P.v) + (size_t)bh * head_elems * C::ESZ;
+  const int kvh = kv_head(bh, P.hq, P.group);
+  const char* kh = reinterpret_cast<const char*>(P.k) + (size_t)kvh * head_elems * C::ESZ;
+  const char* vh = reinterpret_cast<const char*>(P.v) + (size_t)kvh * head_elems * C::ESZ;
   const auto rq = make_rsrc(qh, head_bytes);
   const auto rk = make_rsrc(kh, head_bytes);
   const auto rv = make_rsrc(vh, head_bytes);
@@ -387,8 +388,9 @@ fwd_pipe_kernel(FwdParams P) {
   const size_t head_elems = (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)(head_elems * 2);
   const auto rq = make_rsrc(reinterpret_cast<const char*>(P.q) + (size_t)bh * head_elems * 2, head_bytes);
-  const auto rk = make_rsrc(reinterpret_cast<const char*>(P.k) + (size_t)bh * head_elems * 2, head_bytes);
-  const auto rv = make_rsrc(reinterpret_cast<const char*>(P.v) + (size_t)bh * head_elems * 2, head_bytes);
+  const int kvh = kv_head(bh, P.hq, P.group);
+  const auto rk = make_rsrc(reinterpret_cast<const char*>(P.k) + (size_t)kvh * head_elems * 2, head_bytes);
+  const auto rv = make_rsrc(reinterpret_cast<const char*>(P.v) + (size_t)kvh * head_elems * 2, head_bytes);
   const float sc = P.scale_log2;
   const float tau = P.rescale_log2;
 

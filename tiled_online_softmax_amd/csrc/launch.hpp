@@ -19,12 +19,15 @@ struct FwdParams {
   const float* v_descale;
   int N;
   int causal;
+  int hq;              // query heads per batch entry
+  int group;           // query heads per K/V head (1: one K/V head per query head)
   int n_qtiles;        // set by the launcher
   float scale_log2;    // scale * log2(e)
   float rescale_log2;  // conditional-rescale threshold (base-2 units)
 };
 
 bool fwd_supported(Elt e, int D);
+// H: query heads; K and V have H / p.group heads.
 hipError_t fwd_dispatch(Elt e, int D, const FwdParams& p, int B, int H, hipStream_t st);
 
 struct BwdParams {
@@ -37,17 +40,19 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  float* ld;        // workspace: [B*H*N] lse * log2(e), then [B*H*N] -rowsum(dO * O)
+  float* ld;        // workspace: [B*H*N] lse * log2(e), then [B*H*N] -rowsum(dO * O) (H query heads)
   long long rows;   // B * H * N
   float* dq_accum;  // [B,H,N,D] float workspace (atomic variant), else nullptr
   int N;
   int causal;
+  int hq;            // query heads per batch entry (H above)
+  int group;         // query heads per K/V head
   float scale;       // softmax scale
   float scale_log2;  // scale * log2(e)
 };
 
 bool bwd_supported(int D);
-// variant: 0 atomic, 1 deterministic, 2 dK/dV only (no dQ)
+// variant: 0 atomic, 1 deterministic, 2 dK/dV only (no dQ). H: query heads.
 hipError_t bwd_dispatch(int D, int variant, const BwdParams& p, int B, int H, hipStream_t st);
 
 hipError_t quantize_fp8_launch(const float* x, size_t n, void* codes, float* descale, hipStream_t st);

@@ -21,8 +21,8 @@ FA_F32, FA_BF16, FA_FP8_E4M3 = 0, 1, 2
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, 1, 2, 3, 4
 FA_BWD_ATOMIC, FA_BWD_DETERMINISTIC = 0, 1
 
-EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_fwd_fp8", "fa_quantize_fp8", "fa_bwd_workspace_size", "fa_bwd",
-            "fa_bwd_dkdv", "fa_status_string", "fa_last_error")
+EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_ex", "fa_fwd_fp8", "fa_quantize_fp8", "fa_bwd_workspace_size", "fa_bwd",
+            "fa_bwd_gqa", "fa_bwd_dkdv", "fa_status_string", "fa_last_error")
 
 
 class FAError(RuntimeError):
@@ -43,18 +43,21 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError(f"{LIB_PATH} is not built; run `python -m tiled_online_softmax_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
         L.fa_fwd.argtypes = [_vp] * 5 + [_i] * 5 + [_f, _i, _vp]
+        L.fa_fwd_gqa.argtypes = [_vp] * 5 + [_i] * 6 + [_f, _i, _vp]
         L.fa_fwd_ex.argtypes = [_vp] * 5 + [_i] * 5 + [_f, _i, _f, _vp]
         L.fa_fwd_fp8.argtypes = [_vp] * 5 + [_i] * 5 + [_f] + [_vp] * 3 + [_vp]
         L.fa_quantize_fp8.argtypes = [_vp, _sz, _vp, _vp, _vp]
         L.fa_bwd_workspace_size.argtypes = [_i] * 6
         L.fa_bwd_workspace_size.restype = _sz
         L.fa_bwd.argtypes = [_vp] * 9 + [_i] * 5 + [_f, _i, _i, _vp, _sz, _vp]
+        L.fa_bwd_gqa.argtypes = [_vp] * 9 + [_i] * 6 + [_f, _i, _i, _vp, _sz, _vp]
         L.fa_bwd_dkdv.argtypes = [_vp] * 8 + [_i] * 5 + [_f, _i, _vp, _sz, _vp]
         L.fa_status_string.argtypes = [_i]
         L.fa_status_string.restype = ctypes.c_char_p
         L.fa_last_error.argtypes = []
         L.fa_last_error.restype = ctypes.c_char_p
-        for name in ("fa_fwd", "fa_fwd_ex", "fa_fwd_fp8", "fa_quantize_fp8", "fa_bwd", "fa_bwd_dkdv"):
+        for name in ("fa_fwd", "fa_fwd_gqa", "fa_fwd_ex", "fa_fwd_fp8", "fa_quantize_fp8", "fa_bwd", "fa_bwd_gqa",
+                     "fa_bwd_dkdv"):
             getattr(L, name).restype = _i
         _lib = L
     return _lib
@@ -87,31 +90,50 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def _check_qkv(*ts: torch.Tensor):
+def _check_qkv(*ts: torch.Tensor, kv=()):
+    """q-shaped tensors `ts` and K/V-shaped tensors `kv` (same B, N, D; H a multiple of their head count)."""
     ref = ts[0]
     if ref.dim() != 4:
         raise ValueError("tensors must be [B, H, N, D]")
-    for t in ts:
+    for t in tuple(ts) + tuple(kv):
         if not t.is_cuda:
             raise ValueError("tensors must be on a GPU device")
-        if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device:
-            raise ValueError("q, k, v must share shape, dtype and device")
+        if t.dtype != ref.dtype or t.device != ref.device:
+            raise ValueError("tensors must share dtype and device")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous [B, H, N, D]")
+    for t in ts:
+        if t.shape != ref.shape:
+            raise ValueError("q-shaped tensors must share one shape")
+    if kv:
+        k0 = kv[0]
+        for t in kv:
+            if t.dim() != 4 or t.shape != k0.shape:
+                raise ValueError("k and v must share one shape")
+        B, H, N, D = ref.shape
+        if k0.shape[0] != B or k0.shape[2] != N or k0.shape[3] != D or k0.shape[1] < 1 or H % k0.shape[1]:
+            raise ValueError("k/v must be [B, Hkv, N, D] with Hkv dividing the query heads")
 
 
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False, scale: Optional[float] = None,
         rescale_log2: Optional[float] = None, out: Optional[torch.Tensor] = None,
         lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Attention forward. Returns (O, lse); O is float32 for float32 inputs, bf16 otherwise."""
-    _check_qkv(q, k, v)
+    _check_qkv(q, kv=(k, v))
     B, H, N, D = q.shape
+    Hkv = k.shape[1]
     code = _dtype_code(q)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32 if code == FA_F32 else torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if Hkv != H:
+        if rescale_log2 is not None:
+            raise ValueError("rescale_log2 is only taken with as many K/V heads as query heads")
+        _check(lib().fa_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Hkv,
+                                N, D, int(causal), scale, code, _stream(q)))
+        return out, lse
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, D, int(causal), scale,
             code)
     if rescale_log2 is None:
@@ -162,9 +184,10 @@ def bwd_workspace_size(B: int, H: int, N: int, D: int, variant: int = FA_BWD_ATO
 
 def bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None, variant: int = FA_BWD_ATOMIC,
         workspace: Optional[torch.Tensor] = None, dq=None, dk=None, dv=None):
-    """Attention backward (bf16). Returns (dQ, dK, dV) as bf16 tensors."""
-    _check_qkv(q, k, v, o, do)
+    """Attention backward (bf16). Returns (dQ, dK, dV) as bf16 tensors; dK, dV have k's shape."""
+    _check_qkv(q, o, do, kv=(k, v))
     B, H, N, D = q.shape
+    Hkv = k.shape[1]
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if lse.dtype != torch.float32 or lse.shape != (B, H, N) or not lse.is_contiguous():
         raise ValueError("lse must be contiguous float32 [B, H, N]")
@@ -174,6 +197,12 @@ def bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    if Hkv != H:
+        _check(lib().fa_bwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, D,
+                                int(causal), scale, _dtype_code(q), variant, workspace.data_ptr(), workspace.numel(),
+                                _stream(q)))
+        return dq, dk, dv
     _check(lib().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
                         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, D, int(causal), scale, _dtype_code(q),
                         variant, workspace.data_ptr(), workspace.numel(), _stream(q)))

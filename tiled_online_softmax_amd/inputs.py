@@ -7,7 +7,8 @@ in the HIP library and in the oracle.
 
 Recipe (the same everywhere):
   * generator: numpy ``default_rng(seed)`` (PCG64), ``standard_normal`` in
-    float32, drawn in the order Q, K, V, dO, each of shape [B, H, N, D];
+    float32, drawn in the order Q, K, V, dO; Q and dO have shape [B, H, N, D],
+    K and V [B, Hkv, N, D] (Hkv = H except for grouped-query workloads);
   * an optional multiplier (0.5 for the large-head-dim workload) is applied
     in float32, which is exact for a power of two;
   * bf16 inputs are the round-to-nearest-even bf16 of those float32 values.
@@ -36,6 +37,7 @@ class Workload:
     passes: str  # "fwd" or "bwd"
     multiplier: float = 1.0
     seed: int = SEED_BASE
+    hkv: Optional[int] = None  # K/V heads (grouped-query attention); None means H
 
     @property
     def scale(self) -> float:
@@ -44,6 +46,10 @@ class Workload:
     @property
     def shape(self):
         return (self.B, self.H, self.N, self.D)
+
+    @property
+    def kv_shape(self):
+        return (self.B, self.H if self.hkv is None else self.hkv, self.N, self.D)
 
     def fwd_flops(self) -> float:
         """Two N x N x D contractions (QK^T and PV), 2 flops per FMA; causal is half."""
@@ -63,15 +69,22 @@ WORKLOADS: Dict[str, Workload] = {
     "d256_bf16": Workload("d256_bf16", 1, 8, 8192, 256, "bf16", False, "fwd", multiplier=0.5, seed=SEED_BASE + 3),
     "bwd_causal_bf16": Workload("bwd_causal_bf16", 2, 16, 4096, 64, "bf16", True, "bwd", seed=SEED_BASE + 4),
     "long_fp8_causal": Workload("long_fp8_causal", 1, 32, 32768, 128, "fp8", True, "fwd", seed=SEED_BASE + 5),
+    # Grouped-query attention (a NEXT-row extension): 32 query heads sharing 8 K/V heads.
+    "gqa_causal_bf16": Workload("gqa_causal_bf16", 4, 32, 2048, 128, "bf16", True, "fwd+bwd", seed=SEED_BASE + 6,
+                                hkv=8),
 }
 
 
-def draw(shape, seed: int, count: int = 3, multiplier: float = 1.0):
-    """Return ``count`` float32 arrays of ``shape`` (Q, K, V[, dO]) from one PCG64 stream."""
+def draw(shape, seed: int, count: int = 3, multiplier: float = 1.0, kv_shape=None):
+    """Return ``count`` float32 arrays (Q, K, V[, dO]) from one PCG64 stream.
+
+    Q and dO have ``shape``; K and V have ``kv_shape`` (default ``shape``).
+    """
     rng = np.random.default_rng(seed)
+    shapes = [shape, kv_shape or shape, kv_shape or shape, shape][:count]
     out = []
-    for _ in range(count):
-        x = rng.standard_normal(size=shape, dtype=np.float32)
+    for shp in shapes:
+        x = rng.standard_normal(size=shp, dtype=np.float32)
         if multiplier != 1.0:
             x = x * np.float32(multiplier)
         out.append(x)
@@ -97,7 +110,7 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def make(w: Workload, with_grad: Optional[bool] = None, seed: Optional[int] = None, shape=None):
+def make(w: Workload, with_grad: Optional[bool] = None, seed: Optional[int] = None, shape=None, kv_shape=None):
     """Draw the inputs of workload ``w``.
 
     Returns a dict with float32 draws ``q, k, v`` (and ``do`` for backward
@@ -106,9 +119,10 @@ def make(w: Workload, with_grad: Optional[bool] = None, seed: Optional[int] = No
     parity cases that keep the same value distribution).
     """
     if with_grad is None:
-        with_grad = w.passes == "bwd"
+        with_grad = w.passes != "fwd"
     shp = tuple(shape) if shape is not None else w.shape
-    arrs = draw(shp, w.seed if seed is None else seed, 4 if with_grad else 3, w.multiplier)
+    kv = tuple(kv_shape) if kv_shape is not None else (None if shape is not None else w.kv_shape)
+    arrs = draw(shp, w.seed if seed is None else seed, 4 if with_grad else 3, w.multiplier, kv_shape=kv)
     names = ["q", "k", "v", "do"][: len(arrs)]
     out = dict(zip(names, arrs))
     if w.dtype == "bf16":
