@@ -7,8 +7,16 @@ Conventions (the pages fix none of them; these are the plainest readings):
     dividing H; query head h then uses K/V head h // (H // Hkv), i.e. each run
     of H // Hkv consecutive query heads shares one K/V head;
   * scores are s_ij = scale * <q_i, k_j>;
-  * causal keeps key j only when j <= i (with equal query and key lengths the
-    top-left and bottom-right alignments coincide, and no row is empty);
+  * causal keeps key j only when j <= i + (N_k - N_q): the last query is
+    aligned with the last key (bottom-right), as when queries extend a cached
+    prefix of keys (the KV-cache prefill named in the FlashPrefill V2 entry of
+    the page "FlashAttention" entity trail, section "Corpus findings"); with
+    equal lengths this is j <= i. Causal needs N_k >= N_q, so no row is empty;
+  * a left window w >= 0 also drops keys j < i + (N_k - N_q) - w, i.e. a row
+    keeps at most the w + 1 keys ending at its diagonal (the local
+    sliding-window attention of the WAND entry on the "attention mechanism"
+    tag page, and the local window of the NanoGPT speedrun post on the "MHA"
+    search page); w < 0 means no window;
   * lse_i = log(sum_j exp(s_ij)) with the natural logarithm, over the kept keys.
 
 The method on the pages (tiling, online softmax, deferred normalisation,
@@ -34,6 +42,11 @@ def _row_blocks(n_rows, n_cols):
         yield r0, min(n_rows, r0 + rows)
 
 
+def _check_lengths(n_q, n_k, causal):
+    if causal and n_k < n_q:
+        raise ValueError(f"causal attention needs at least as many keys ({n_k}) as queries ({n_q})")
+
+
 def _group(h_q, h_kv):
     """Query heads per K/V head; H_kv must divide H_q."""
     if h_kv < 1 or h_q % h_kv:
@@ -41,17 +54,30 @@ def _group(h_q, h_kv):
     return h_q // h_kv
 
 
-def scores(q, k, scale, causal, rows=None):
+def key_bounds(rows, n_q, n_k, causal, window=-1):
+    """First and last key index each query row keeps (inclusive), per the conventions above."""
+    rows = np.asarray(rows, dtype=np.int64)
+    off = n_k - n_q
+    lo = np.maximum(0, rows + off - window) if window >= 0 else np.zeros_like(rows)
+    hi = np.minimum(n_k - 1, rows + off) if causal else np.full_like(rows, n_k - 1)
+    return lo, hi
+
+
+def scores(q, k, scale, causal, rows=None, n_q=None, window=-1):
     """S[i, j] = scale * q_i . k_j for one head, masked entries set to -inf.
 
-    q: [M, D] (the query rows listed in ``rows``, or all rows 0..M-1), k: [N, D].
+    q: [M, D] (the query rows listed in ``rows``, or all rows 0..M-1), k: [N_k, D];
+    n_q: the head's query length (default M).
     """
     q = _as_f64(q)
     k = _as_f64(k)
     s = scale * (q @ k.T)
-    if causal:
-        idx = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
-        s = np.where(np.arange(k.shape[0])[None, :] > idx[:, None], -np.inf, s)
+    idx = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+    n_q = q.shape[0] if n_q is None else n_q
+    if causal or window >= 0:
+        lo, hi = key_bounds(idx, n_q, k.shape[0], causal, window)
+        j = np.arange(k.shape[0])[None, :]
+        s = np.where((j < lo[:, None]) | (j > hi[:, None]), -np.inf, s)
     return s
 
 
@@ -63,14 +89,15 @@ def softmax_rows(s):
     return p / l[:, None], m + np.log(l)
 
 
-def forward(q, k, v, causal, scale, rows=None):
+def forward(q, k, v, causal, scale, rows=None, window=-1):
     """Attention forward for all heads.
 
     Args:
-      q: [B, H, N, D]; k, v: [B, Hkv, N, D] with Hkv dividing H (any float
+      q: [B, H, N_q, D]; k, v: [B, Hkv, N_k, D] with Hkv dividing H (any float
         dtype; widened to float64).
-      causal: keep key j only for j <= i.
+      causal: keep key j only for j <= i + N_k - N_q.
       scale: the factor on q.k.
+      window: left window (keys j >= i + N_k - N_q - window), < 0 for none.
       rows: optional sorted 1-D array of query indices; when given, only those
         rows are computed (rows are independent, so this is the same result).
     Returns:
@@ -81,6 +108,7 @@ def forward(q, k, v, causal, scale, rows=None):
     v = _as_f64(v)
     B, H, N, D = q.shape
     G = _group(H, k.shape[1])
+    _check_lengths(N, k.shape[2], causal)
     sel = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
     M = sel.shape[0]
     o = np.empty((B, H, M, v.shape[-1]))
@@ -90,14 +118,14 @@ def forward(q, k, v, causal, scale, rows=None):
             kh = h // G
             for r0, r1 in _row_blocks(M, k.shape[2]):
                 rr = sel[r0:r1]
-                s = scores(q[b, h, rr], k[b, kh], scale, causal, rows=rr)
+                s = scores(q[b, h, rr], k[b, kh], scale, causal, rows=rr, n_q=N, window=window)
                 p, lse_blk = softmax_rows(s)
                 o[b, h, r0:r1] = p @ v[b, kh]
                 lse[b, h, r0:r1] = lse_blk
     return o, lse
 
 
-def backward(q, k, v, do, causal, scale):
+def backward(q, k, v, do, causal, scale, window=-1):
     """Gradients of sum(dO * O) with respect to Q, K and V, in float64.
 
     Follows the chain rule through the definition O = softmax(S) V with
@@ -120,10 +148,11 @@ def backward(q, k, v, do, causal, scale):
     dv = np.zeros_like(v)
     B, H, N, D = q.shape
     G = _group(H, k.shape[1])
+    _check_lengths(N, k.shape[2], causal)
     for b in range(B):
         for h in range(H):
             kh = h // G
-            s = scores(q[b, h], k[b, kh], scale, causal)
+            s = scores(q[b, h], k[b, kh], scale, causal, window=window)
             p, _ = softmax_rows(s)
             dv[b, kh] += p.T @ do[b, h]
             dp = do[b, h] @ v[b, kh].T

@@ -13,12 +13,20 @@ def _dot(a, b):
     return math.fsum(x * y for x, y in zip(a, b))
 
 
-def forward(q, k, v, causal, scale):
-    """q, k, v: nested lists [N][D] of floats for one head. Returns (O [N][D], lse [N])."""
+def _keys(i, n_q, n_k, causal, window):
+    """Keys row i keeps: from i + (n_k - n_q) - window (or 0) up to i + (n_k - n_q) (or the last key)."""
+    diag = i + n_k - n_q
+    first = max(0, diag - window) if window >= 0 else 0
+    last = min(n_k - 1, diag) if causal else n_k - 1
+    return list(range(first, last + 1))
+
+
+def forward(q, k, v, causal, scale, window=-1):
+    """q: nested list [N_q][D], k, v: [N_k][D] floats for one head. Returns (O [N_q][D], lse [N_q])."""
     n = len(q)
     o, lse = [], []
     for i in range(n):
-        keys = [j for j in range(len(k)) if not (causal and j > i)]
+        keys = _keys(i, n, len(k), causal, window)
         s = [scale * _dot(q[i], k[j]) for j in keys]
         m = max(s)
         e = [math.exp(x - m) for x in s]
@@ -28,13 +36,14 @@ def forward(q, k, v, causal, scale):
     return o, lse
 
 
-def backward(q, k, v, do, causal, scale):
+def backward(q, k, v, do, causal, scale, window=-1):
     """Loop form of dQ, dK, dV for one head (nested lists)."""
     n, dd = len(q), len(q[0])
     nk = len(k)
     p = []
     for i in range(n):
-        s = [(-math.inf if (causal and j > i) else scale * _dot(q[i], k[j])) for j in range(nk)]
+        kept = set(_keys(i, n, nk, causal, window))
+        s = [(scale * _dot(q[i], k[j]) if j in kept else -math.inf) for j in range(nk)]
         m = max(s)
         e = [0.0 if x == -math.inf else math.exp(x - m) for x in s]
         l = math.fsum(e)

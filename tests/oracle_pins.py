@@ -19,6 +19,11 @@ own code:
   * central finite differences of the forward for the backward;
   * exact backward identities: sum_j dK_j = 0, sum_j dV_j = sum_i dO_i, and
     dQ = dK = 0 when all value rows are equal;
+  * query and key lengths that differ, with the causal diagonal aligned at
+    the bottom right: torch's causal_lower_right attention bias and autograd;
+  * left windows: closed forms (a zero window keeps exactly the diagonal key;
+    a window covering every key changes nothing) and, row by row, plain
+    attention over the slice of keys the window keeps;
   * grouped K/V heads: torch's scaled_dot_product_attention with enable_gqa
     and its autograd, and the identity that a group's shared K/V head gives
     the same outputs as every query head holding its own copy (whose dK and dV
@@ -266,6 +271,98 @@ def pin_gqa_matches_copied_heads(fwd, bwd, tol=1e-12):
         np.testing.assert_allclose(dq, dq_r, atol=tol)
         np.testing.assert_allclose(dk, dk_r.reshape(B, Hkv, G, N, D).sum(axis=2), atol=tol)
         np.testing.assert_allclose(dv, dv_r.reshape(B, Hkv, G, N, D).sum(axis=2), atol=tol)
+
+
+def pin_torch_lower_right(fwd, bwd, tol=1e-11):
+    """torch CPU float64 sdpa with the causal_lower_right bias (a library routine), N_q != N_k, and its autograd."""
+    import torch
+    from torch.nn.attention.bias import causal_lower_right
+
+    for (B, H, Nq, Nk, D, causal, seed) in [(1, 2, 7, 19, 8, True, 80), (2, 1, 16, 16, 8, True, 81),
+                                              (1, 2, 23, 9, 16, False, 82), (1, 1, 1, 30, 8, True, 83)]:
+        q, do = _rand((B, H, Nq, D), seed), _rand((B, H, Nq, D), seed + 3)
+        k, v = _rand((B, H, Nk, D), seed + 1), _rand((B, H, Nk, D), seed + 2)
+        scale = 0.3
+        o, lse = fwd(q, k, v, causal, scale)
+        tq, tk, tv = (torch.from_numpy(x).requires_grad_() for x in (q, k, v))
+        mask = causal_lower_right(Nq, Nk) if causal else None
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=scale)
+        np.testing.assert_allclose(o, ref.detach().numpy(), atol=tol)
+        s = scale * (tq @ tk.transpose(-1, -2))
+        if causal:
+            s = s.masked_fill(~causal_lower_right(Nq, Nk)._materialize(), float("-inf"))
+        np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).detach().numpy(), atol=tol)
+        ref.backward(torch.from_numpy(do))
+        dq, dk, dv = bwd(q, k, v, do, causal, scale)
+        for mine, theirs in ((dq, tq), (dk, tk), (dv, tv)):
+            np.testing.assert_allclose(mine, theirs.grad.numpy(), atol=tol)
+
+
+def pin_window_closed_forms(fwd, tol=1e-12):
+    """Window 0 (causal) keeps only key i + N_k - N_q: O_i = v_that, lse_i = its score. A window
+    covering every key is no window."""
+    for (Nq, Nk) in [(13, 13), (5, 21)]:
+        q, k, v = _rand((1, 2, Nq, 8), 90), _rand((1, 2, Nk, 8), 91), _rand((1, 2, Nk, 8), 92)
+        off = Nk - Nq
+        o, lse = fwd(q, k, v, True, 0.7, window=0)
+        diag = np.arange(Nq) + off
+        np.testing.assert_allclose(o, v[:, :, diag], atol=tol)
+        np.testing.assert_allclose(lse, 0.7 * np.einsum("bhnd,bhnd->bhn", q, k[:, :, diag]), atol=tol)
+        for causal in (False, True):
+            o_w, lse_w = fwd(q, k, v, causal, 0.7, window=Nk + Nq)
+            o_n, lse_n = fwd(q, k, v, causal, 0.7)
+            np.testing.assert_allclose(o_w, o_n, atol=tol)
+            np.testing.assert_allclose(lse_w, lse_n, atol=tol)
+
+
+def pin_window_equals_key_slice(fwd, tol=1e-12):
+    """Row i of windowed attention equals plain (unmasked) attention of q_i over the keys it keeps."""
+    for (Nq, Nk, causal, w) in [(40, 40, True, 7), (11, 37, True, 15), (25, 25, False, 5)]:
+        q, k, v = _rand((1, 1, Nq, 8), 100 + w), _rand((1, 1, Nk, 8), 101 + w), _rand((1, 1, Nk, 8), 102 + w)
+        o, lse = fwd(q, k, v, causal, 0.5, window=w)
+        for i in range(Nq):
+            diag = i + Nk - Nq
+            first = max(0, diag - w)
+            last = min(Nk - 1, diag) if causal else Nk - 1
+            ks, vs = k[:, :, first:last + 1], v[:, :, first:last + 1]
+            o_i, lse_i = fwd(q[:, :, i:i + 1], ks, vs, False, 0.5)
+            np.testing.assert_allclose(o[:, :, i:i + 1], o_i, atol=tol)
+            np.testing.assert_allclose(lse[:, :, i:i + 1], lse_i, atol=tol)
+
+
+def pin_brute_force_masks(fwd, bwd, brute, tol=1e-12):
+    """The scalar-loop oracle with N_q != N_k and windows, forward and backward, on tiny heads."""
+    for (Nq, Nk, causal, w, seed) in [(5, 9, True, 2, 110), (7, 7, True, 0, 111), (6, 4, False, 1, 112),
+                                       (3, 11, True, -1, 113), (8, 8, False, 3, 114)]:
+        q, do = _rand((1, 1, Nq, 4), seed), _rand((1, 1, Nq, 4), seed + 3)
+        k, v = _rand((1, 1, Nk, 4), seed + 1), _rand((1, 1, Nk, 4), seed + 2)
+        o, lse = fwd(q, k, v, causal, 0.6, window=w)
+        o_b, lse_b = brute.forward(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), causal, 0.6, window=w)
+        np.testing.assert_allclose(o[0, 0], np.array(o_b), atol=tol)
+        np.testing.assert_allclose(lse[0, 0], np.array(lse_b), atol=tol)
+        g = bwd(q, k, v, do, causal, 0.6, window=w)
+        g_b = brute.backward(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), do[0, 0].tolist(), causal, 0.6,
+                             window=w)
+        for a, b in zip(g, g_b):
+            np.testing.assert_allclose(a[0, 0], np.array(b), atol=tol)
+
+
+def pin_finite_differences_masks(fwd, bwd, tol=1e-7):
+    """Central differences of sum(dO * O) with N_q != N_k and a window match the backward."""
+    q, do = _rand((1, 1, 4, 3), 120), _rand((1, 1, 4, 3), 123)
+    k, v = _rand((1, 1, 7, 3), 121), _rand((1, 1, 7, 3), 122)
+    causal, w, scale = True, 2, 0.8
+    dq, dk, dv = bwd(q, k, v, do, causal, scale, window=w)
+    eps = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        for idx in np.ndindex(x.shape):
+            x0 = x[idx]
+            x[idx] = x0 + eps
+            lp = float((do * fwd(q, k, v, causal, scale, window=w)[0]).sum())
+            x[idx] = x0 - eps
+            lm = float((do * fwd(q, k, v, causal, scale, window=w)[0]).sum())
+            x[idx] = x0
+            assert abs((lp - lm) / (2 * eps) - g[idx]) <= tol, (idx, (lp - lm) / (2 * eps), g[idx])
 
 
 FORWARD_PINS = [pin_zero_query, pin_constant_scores, pin_ones_value, pin_permutation, pin_key_shift,

@@ -41,6 +41,31 @@ def test_gqa_rejects_bad_groups():
         attention.forward(q, np.zeros((1, 3, 3, 2)), np.zeros((1, 3, 3, 2)), False, 1.0)
 
 
+def test_torch_lower_right():
+    pins.pin_torch_lower_right(attention.forward, attention.backward)
+
+
+def test_window_closed_forms():
+    pins.pin_window_closed_forms(attention.forward)
+
+
+def test_window_equals_key_slice():
+    pins.pin_window_equals_key_slice(attention.forward)
+
+
+def test_brute_force_masks():
+    pins.pin_brute_force_masks(attention.forward, attention.backward, brute)
+
+
+def test_finite_differences_masks():
+    pins.pin_finite_differences_masks(attention.forward, attention.backward)
+
+
+def test_causal_needs_enough_keys():
+    with pytest.raises(ValueError):
+        attention.forward(np.zeros((1, 1, 5, 2)), np.zeros((1, 1, 4, 2)), np.zeros((1, 1, 4, 2)), True, 1.0)
+
+
 def test_brute_force():
     pins.pin_brute_force(attention.forward, attention.backward, brute)
 

@@ -173,3 +173,67 @@ def test_unmutated_gqa_factory_passes():
     fwd, bwd = _gqa_factory()
     pins.pin_torch_gqa(fwd, bwd)
     pins.pin_gqa_matches_copied_heads(fwd, bwd)
+
+
+def _mask_factory(top_left=False, window_short=False):
+    """The oracle with one planted mistake in the key bounds: top-left causal alignment, or a window one key short."""
+    def bounds(rows, n_q, n_k, causal, window):
+        rows = np.asarray(rows)
+        off = 0 if top_left else n_k - n_q
+        w = window - 1 if (window_short and window >= 0) else window
+        lo = np.maximum(0, rows + off - w) if window >= 0 else np.zeros_like(rows)
+        hi = np.minimum(n_k - 1, rows + off) if causal else np.full_like(rows, n_k - 1)
+        return lo, hi
+
+    def head(q, k, causal, scale, window):
+        s = scale * (q @ k.T)
+        lo, hi = bounds(np.arange(q.shape[0]), q.shape[0], k.shape[0], causal, window)
+        j = np.arange(k.shape[0])[None, :]
+        return np.where((j < lo[:, None]) | (j > hi[:, None]), -np.inf, s)
+
+    def fwd(q, k, v, causal, scale, rows=None, window=-1):
+        q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+        B, H, N, _ = q.shape
+        o, lse = np.empty((B, H, N, v.shape[-1])), np.empty((B, H, N))
+        for b in range(B):
+            for h in range(H):
+                p, lse[b, h] = attention.softmax_rows(head(q[b, h], k[b, h], causal, scale, window))
+                o[b, h] = p @ v[b, h]
+        return o, lse
+
+    def bwd(q, k, v, do, causal, scale, window=-1):
+        q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+        dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+        B, H = q.shape[:2]
+        for b in range(B):
+            for h in range(H):
+                p, _ = attention.softmax_rows(head(q[b, h], k[b, h], causal, scale, window))
+                dv[b, h] = p.T @ do[b, h]
+                dp = do[b, h] @ v[b, h].T
+                ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+                dq[b, h] = scale * (ds @ k[b, h])
+                dk[b, h] = scale * (ds.T @ q[b, h])
+        return dq, dk, dv
+    return fwd, bwd
+
+
+@pytest.mark.parametrize("mutant", ["top_left_causal", "window_one_short"])
+def test_mask_mutants_fail_a_pin(mutant):
+    fwd, bwd = _mask_factory(top_left=mutant == "top_left_causal", window_short=mutant == "window_one_short")
+    checks = [lambda: pins.pin_torch_lower_right(fwd, bwd), lambda: pins.pin_window_closed_forms(fwd),
+              lambda: pins.pin_window_equals_key_slice(fwd), lambda: pins.pin_brute_force_masks(fwd, bwd, brute)]
+    failures = 0
+    for c in checks:
+        try:
+            c()
+        except (AssertionError, ValueError):
+            failures += 1
+    assert failures >= 1
+
+
+def test_unmutated_mask_factory_passes():
+    fwd, bwd = _mask_factory()
+    pins.pin_torch_lower_right(fwd, bwd)
+    pins.pin_window_closed_forms(fwd)
+    pins.pin_window_equals_key_slice(fwd)
+    pins.pin_brute_force_masks(fwd, bwd, brute)
