@@ -19,7 +19,9 @@
  * (Metal Port)" README, section "Documentation").
  *
  * Layout: Q, K, V, O, dO, dQ, dK, dV are contiguous row-major [B, H, N, D];
- * lse is contiguous float32 [B, H, N]. Query and key lengths are equal.
+ * lse is contiguous float32 [B, H, N]. Query and key lengths are equal except
+ * in fa_fwd_general / fa_bwd_general, and K/V heads may be fewer than query
+ * heads in the _gqa and _general entry points.
  *
  * Ownership: the caller allocates and owns every buffer (device memory).
  * The library never allocates, frees or synchronises, and keeps no state
@@ -92,6 +94,29 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int Hkv, int N, int D, int causal, float scale,
                int dtype, void* stream);
+
+/*
+ * General forward: grouped K/V heads (as fa_fwd_gqa), query and key lengths
+ * that differ, and an optional left window.
+ *   q, o   : [B, H, Nq, D];  k, v : [B, Hkv, Nk, D];  lse : [B, H, Nq].
+ *   causal : 1 keeps key j for query i only if j <= i + (Nk - Nq): the causal
+ *            diagonal is aligned at the bottom right, so the last query sees
+ *            every key, as when new queries extend a cached prefix of keys
+ *            (the KV-cache prefill of the FlashPrefill V2 entry on the
+ *            "FlashAttention" entity trail page, section "Corpus findings").
+ *            Needs Nk >= Nq (otherwise the first rows would keep no key).
+ *   window : -1, or w >= 0 to keep only keys j >= i + (Nk - Nq) - w -- with
+ *            causal, a sliding window of the w + 1 keys ending at the
+ *            diagonal (the local sliding-window attention of the WAND entry
+ *            on the "attention mechanism" tag page). Tiles wholly outside a
+ *            row's keys are skipped.
+ * Nq = Nk = N with window = -1 is fa_fwd_gqa. Other arguments as for
+ * fa_fwd; FA_ERR_INVALID_ARG also for Nk < 1, a K/V head of 2^31 bytes or
+ * more, causal with Nk < Nq, or window < -1.
+ */
+int fa_fwd_general(const void* q, const void* k, const void* v, void* o,
+                   float* lse, int B, int H, int Hkv, int Nq, int Nk, int D,
+                   int causal, int window, float scale, int dtype, void* stream);
 
 /*
  * fa_fwd with an explicit conditional-rescale threshold `rescale_log2`
@@ -186,6 +211,20 @@ int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
                int B, int H, int Hkv, int N, int D, int causal, float scale,
                int dtype, int variant, void* workspace, size_t workspace_bytes,
                void* stream);
+
+/*
+ * General backward: the gradients of fa_fwd_general.
+ *   q, o, dO, dq : [B, H, Nq, D];  k, v, dk, dv : [B, Hkv, Nk, D];
+ *   lse          : [B, H, Nq];  workspace: fa_bwd_workspace_size(B, H, Nq, D,
+ *                  dtype, variant) bytes.
+ * Keys that no query keeps (possible under a window) get dK = dV = 0. Other
+ * arguments, variants and errors as for fa_bwd_gqa and fa_fwd_general.
+ */
+int fa_bwd_general(const void* q, const void* k, const void* v, const void* o,
+                   const void* dO, const float* lse, void* dq, void* dk,
+                   void* dv, int B, int H, int Hkv, int Nq, int Nk, int D,
+                   int causal, int window, float scale, int dtype, int variant,
+                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * dK and dV only: the preprocess and the key-tile pass of fa_bwd, without any

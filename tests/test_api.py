@@ -182,3 +182,53 @@ def test_bwd_gqa_validation():
     # 64 query heads of 2^20 x 64 bf16 (2^27 bytes each) share one K/V head: the group spans 2^33 bytes
     big = fa.bwd_workspace_size(1, 64, 1 << 20, 64, fa.FA_BWD_DETERMINISTIC)
     assert call(64, 1, N=1 << 20, wsb=big) == fa.FA_ERR_UNSUPPORTED and "2^32" in fa.last_error()
+
+
+def _fwd_general(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, Hkv=1, Nq=16, Nk=32, D=64, causal=1, window=-1, scale=0.125,
+             dtype=fa.FA_BF16)
+    a.update(kw)
+    return fa.lib().fa_fwd_general(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["Nq"],
+                                   a["Nk"], a["D"], a["causal"], a["window"], a["scale"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(Nk=0), fa.FA_ERR_INVALID_ARG, "Nk"),
+    (dict(Nq=0), fa.FA_ERR_INVALID_ARG, ">= 1"),
+    (dict(Nq=40, Nk=32, causal=1), fa.FA_ERR_INVALID_ARG, "Nk >= Nq"),
+    (dict(window=-2), fa.FA_ERR_INVALID_ARG, "window"),
+    (dict(Hkv=3), fa.FA_ERR_INVALID_ARG, "divide"),
+    (dict(Nk=1 << 24, D=128, Nq=16), fa.FA_ERR_INVALID_ARG, "2^31"),
+    (dict(D=96), fa.FA_ERR_UNSUPPORTED, "D=96"),
+    (dict(k=None), fa.FA_ERR_INVALID_ARG, "NULL"),
+])
+def test_fwd_general_validation(kw, status, msg):
+    assert _fwd_general(**kw) == status
+    assert msg in fa.last_error()
+
+
+def test_bwd_general_validation():
+    L = fa.lib()
+    ws = fa.bwd_workspace_size(1, 2, 16, 64, fa.FA_BWD_DETERMINISTIC)
+
+    def call(Nq=16, Nk=32, causal=1, window=-1, variant=fa.FA_BWD_DETERMINISTIC, wsb=ws, dtype=fa.FA_BF16):
+        return L.fa_bwd_general(P, P, P, P, P, P, P, P, P, 1, 2, 1, Nq, Nk, 64, causal, window, 0.1, dtype, variant,
+                                P, wsb, None)
+
+    assert call(Nq=40, Nk=32) == fa.FA_ERR_INVALID_ARG and "Nk >= Nq" in fa.last_error()
+    assert call(window=-5) == fa.FA_ERR_INVALID_ARG and "window" in fa.last_error()
+    assert call(Nk=0) == fa.FA_ERR_INVALID_ARG
+    assert call(variant=2) == fa.FA_ERR_INVALID_ARG
+    assert call(wsb=ws - 1) == fa.FA_ERR_WORKSPACE
+    assert call(dtype=fa.FA_F32) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_binding_argument_counts_match_header():
+    """Every ctypes prototype in the binding has as many arguments as the declaration in include/fa.h."""
+    text = open(os.path.join(ROOT, "include", "fa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    L = fa.lib()
+    for name, params in re.findall(r"\b(fa_[a-z0-9_]+)\s*\(([^)]*)\)\s*;", text):
+        params = params.strip()
+        n = 0 if params in ("", "void") else len(params.split(","))
+        assert len(getattr(L, name).argtypes) == n, (name, n, len(getattr(L, name).argtypes))

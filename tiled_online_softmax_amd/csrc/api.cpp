@@ -72,13 +72,23 @@ int check_heads(int H, int Hkv) {
   return FA_OK;
 }
 
-int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N, int D,
-             int causal, float scale, int dtype, float rescale_log2, const float* dq, const float* dk,
-             const float* dv, void* stream) {
+// Key length Nk (queries N) and the left window: checks shared by the forward and backward.
+int check_keys(int N, int Nk, int D, int causal, int window, int esz) {
+  if (Nk < 1) return fail(FA_ERR_INVALID_ARG, "Nk must be >= 1 (got %d)", Nk);
+  if ((long long)Nk * D * esz >= (1LL << 31)) return fail(FA_ERR_INVALID_ARG, "one K/V head (Nk*D*elem = %lld bytes) must be < 2^31 bytes", (long long)Nk * D * esz);
+  if (causal && Nk < N) return fail(FA_ERR_INVALID_ARG, "causal attention needs Nk >= Nq (got Nq=%d, Nk=%d): the first rows would keep no key", N, Nk);
+  if (window < -1) return fail(FA_ERR_INVALID_ARG, "window must be -1 (none) or >= 0 (got %d)", window);
+  return FA_OK;
+}
+
+int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N, int Nk,
+             int D, int causal, int window, float scale, int dtype, float rescale_log2, const float* dq,
+             const float* dk, const float* dv, void* stream) {
   const int esz = dtype_bytes(dtype);
   if (!esz) return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
   if (int s = check_common(B, H, N, D, causal, scale, esz)) return s;
   if (int s = check_heads(H, Hkv)) return s;
+  if (int s = check_keys(N, Nk, D, causal, window, esz)) return s;
   if (!std::isfinite(rescale_log2) || rescale_log2 < 0.f)
     return fail(FA_ERR_INVALID_ARG, "rescale threshold must be finite and >= 0 (got %g)", (double)rescale_log2);
   if (int s = check_ptrs({q, k, v, o, lse})) return s;
@@ -87,7 +97,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   fa::FwdParams p{};
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
   p.q_descale = dq; p.k_descale = dk; p.v_descale = dv;
-  p.N = N; p.causal = causal;
+  p.N = N; p.Nk = Nk; p.causal = causal; p.window = window;
   p.hq = H; p.group = H / Hkv;
   p.scale_log2 = scale * fa::kLog2e;
   p.rescale_log2 = rescale_log2;
@@ -100,18 +110,26 @@ extern "C" {
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int D, int causal,
            float scale, int dtype, void* stream) {
-  return fwd_impl(q, k, v, o, lse, B, H, H, N, D, causal, scale, dtype, 8.0f, nullptr, nullptr, nullptr, stream);
+  return fwd_impl(q, k, v, o, lse, B, H, H, N, N, D, causal, -1, scale, dtype, 8.0f, nullptr, nullptr, nullptr,
+                  stream);
 }
 
 int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N, int D,
                int causal, float scale, int dtype, void* stream) {
-  return fwd_impl(q, k, v, o, lse, B, H, Hkv, N, D, causal, scale, dtype, 8.0f, nullptr, nullptr, nullptr, stream);
+  return fwd_impl(q, k, v, o, lse, B, H, Hkv, N, N, D, causal, -1, scale, dtype, 8.0f, nullptr, nullptr, nullptr,
+                  stream);
+}
+
+int fa_fwd_general(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int Nq,
+                   int Nk, int D, int causal, int window, float scale, int dtype, void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, H, Hkv, Nq, Nk, D, causal, window, scale, dtype, 8.0f, nullptr, nullptr,
+                  nullptr, stream);
 }
 
 int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int D,
               int causal, float scale, int dtype, float rescale_log2, void* stream) {
-  return fwd_impl(q, k, v, o, lse, B, H, H, N, D, causal, scale, dtype, rescale_log2, nullptr, nullptr, nullptr,
-                  stream);
+  return fwd_impl(q, k, v, o, lse, B, H, H, N, N, D, causal, -1, scale, dtype, rescale_log2, nullptr, nullptr,
+                  nullptr, stream);
 }
 
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int D,
@@ -119,8 +137,8 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                void* stream) {
   for (const float* d : {q_descale, k_descale, v_descale})
     if (d && (reinterpret_cast<uintptr_t>(d) & 3u)) return fail(FA_ERR_INVALID_ARG, "descale pointer not 4-byte aligned");
-  return fwd_impl(q, k, v, o, lse, B, H, H, N, D, causal, scale, FA_FP8_E4M3, 0.0f, q_descale, k_descale, v_descale,
-                  stream);
+  return fwd_impl(q, k, v, o, lse, B, H, H, N, N, D, causal, -1, scale, FA_FP8_E4M3, 0.0f, q_descale, k_descale,
+                  v_descale, stream);
 }
 
 int fa_quantize_fp8(const float* x, size_t n, void* codes, float* descale, void* stream) {
@@ -146,14 +164,15 @@ namespace {
 
 // Shared by fa_bwd and fa_bwd_dkdv; variant 2 is the dK/dV-only pass.
 int bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse, void* dq,
-             void* dk, void* dv, int B, int H, int Hkv, int N, int D, int causal, float scale, int dtype, int variant,
-             void* workspace, size_t workspace_bytes, void* stream) {
+             void* dk, void* dv, int B, int H, int Hkv, int N, int Nk, int D, int causal, int window, float scale,
+             int dtype, int variant, void* workspace, size_t workspace_bytes, void* stream) {
   if (dtype != FA_BF16) {
     if (!dtype_bytes(dtype)) return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
     return fail(FA_ERR_UNSUPPORTED, "backward is built for FA_BF16 only (got dtype %d)", dtype);
   }
   if (int s = check_common(B, H, N, D, causal, scale, 2)) return s;
   if (int s = check_heads(H, Hkv)) return s;
+  if (int s = check_keys(N, Nk, D, causal, window, 2)) return s;
   if ((long long)(H / Hkv) * N * D * 2 >= (1LL << 32))
     return fail(FA_ERR_UNSUPPORTED, "backward: the %d query heads sharing a K/V head must span < 2^32 bytes", H / Hkv);
   if (variant != FA_BWD_ATOMIC && variant != FA_BWD_DETERMINISTIC && variant != 2)
@@ -176,7 +195,8 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
   p.dq_accum = variant == FA_BWD_ATOMIC
                    ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + ((rows * 2 * sizeof(float) + 255) & ~(size_t)255))
                    : nullptr;
-  p.N = N; p.causal = causal; p.scale = scale; p.scale_log2 = scale * fa::kLog2e;
+  p.N = N; p.Nk = Nk; p.causal = causal; p.window = window;
+  p.scale = scale; p.scale_log2 = scale * fa::kLog2e;
   p.hq = H; p.group = H / Hkv;
   p.rows = (long long)rows;
   return hip_status(fa::bwd_dispatch(D, variant, p, B, H, reinterpret_cast<hipStream_t>(stream)), "fa_bwd launch");
@@ -191,7 +211,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            void* workspace, size_t workspace_bytes, void* stream) {
   if (variant != FA_BWD_ATOMIC && variant != FA_BWD_DETERMINISTIC)
     return fail(FA_ERR_INVALID_ARG, "variant must be FA_BWD_ATOMIC or FA_BWD_DETERMINISTIC (got %d)", variant);
-  return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, B, H, H, N, D, causal, scale, dtype, variant, workspace,
+  return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, B, H, H, N, N, D, causal, -1, scale, dtype, variant, workspace,
                   workspace_bytes, stream);
 }
 
@@ -200,14 +220,23 @@ int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const
                int variant, void* workspace, size_t workspace_bytes, void* stream) {
   if (variant != FA_BWD_ATOMIC && variant != FA_BWD_DETERMINISTIC)
     return fail(FA_ERR_INVALID_ARG, "variant must be FA_BWD_ATOMIC or FA_BWD_DETERMINISTIC (got %d)", variant);
-  return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, B, H, Hkv, N, D, causal, scale, dtype, variant, workspace,
+  return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, B, H, Hkv, N, N, D, causal, -1, scale, dtype, variant, workspace,
                   workspace_bytes, stream);
+}
+
+int fa_bwd_general(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                   void* dq, void* dk, void* dv, int B, int H, int Hkv, int Nq, int Nk, int D, int causal, int window,
+                   float scale, int dtype, int variant, void* workspace, size_t workspace_bytes, void* stream) {
+  if (variant != FA_BWD_ATOMIC && variant != FA_BWD_DETERMINISTIC)
+    return fail(FA_ERR_INVALID_ARG, "variant must be FA_BWD_ATOMIC or FA_BWD_DETERMINISTIC (got %d)", variant);
+  return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, B, H, Hkv, Nq, Nk, D, causal, window, scale, dtype, variant,
+                  workspace, workspace_bytes, stream);
 }
 
 int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
                 void* dk, void* dv, int B, int H, int N, int D, int causal, float scale, int dtype, void* workspace,
                 size_t workspace_bytes, void* stream) {
-  return bwd_impl(q, k, v, o, dO, lse, nullptr, dk, dv, B, H, H, N, D, causal, scale, dtype, 2, workspace,
+  return bwd_impl(q, k, v, o, dO, lse, nullptr, dk, dv, B, H, H, N, N, D, causal, -1, scale, dtype, 2, workspace,
                   workspace_bytes, stream);
 }
 

@@ -121,7 +121,8 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
   // dV contributions in the accumulators.
   int bh, kt;
   wg_map(n_ktiles, P.causal, bh, kt);
-  const int N = P.N;
+  const int N = P.N;  // query rows per head
+  const KeyBounds kb{N, P.Nk, P.causal, P.window};
   const int group = P.group;
   const int hkv = P.hq / group;
   const int qbh0 = (bh / hkv) * P.hq + (bh % hkv) * group;
@@ -129,9 +130,9 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
   const int kw = k0 + 32 * wave;
   const int key = kw + li;
 
-  const size_t head = (size_t)bh * N * D;        // K/V head
+  const size_t head = (size_t)bh * P.Nk * D;     // K/V head
   const size_t qhead = (size_t)qbh0 * N * D;     // first query head of the group
-  const uint32_t head_bytes = (uint32_t)((size_t)N * D * 2);
+  const uint32_t head_bytes = (uint32_t)((size_t)P.Nk * D * 2);
   const uint32_t group_bytes = (uint32_t)((size_t)group * N * D * 2);
   const auto rq = make_rsrc(reinterpret_cast<const __bf16*>(P.q) + qhead, group_bytes);
   const auto rk = make_rsrc(reinterpret_cast<const __bf16*>(P.k) + head, head_bytes);
@@ -199,8 +200,9 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
     adv[e] = f32x16{};
   }
 
-  const int qt0 = P.causal ? k0 / BQ : 0;
-  const int nq = (N + BQ - 1) / BQ;
+  // query tiles [qt0, nq) hold every query that keeps a key of this workgroup
+  const int qt0 = kb.qlo(k0) / BQ;
+  const int nq = kb.qhi(min(k0 + C::BK, P.Nk) - 1) / BQ + 1;
   const float sl2 = P.scale_log2;
 
   // Query tiles visited, head by head of the group: (hg, it) runs over
@@ -212,8 +214,11 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
       ++g;
     }
   };
-  issue(qt0 * BQ, smem);
-  wait_vmem();
+  // (a window can leave the first keys with no query at all: then dK = dV = 0)
+  if (qt0 < nq) {
+    issue(qt0 * BQ, smem);
+    wait_vmem();
+  }
   __syncthreads();
 
   // One query tile. `cur` is read while the LDS-DMA prefetch fills `nxt`; the
@@ -234,7 +239,7 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
     opaque(qbase);
     opaque(tbase);
 
-    const bool live = !P.causal || q0 + BQ - 1 >= kw;
+    const bool live = q0 + BQ - 1 >= kb.qlo(kw) && q0 <= kb.qhi(kw + 31);
     bf16x8 pb[BQ / 16], db[BQ / 16];  // P and dS as bf16 B operands, 16 queries per piece
     if (live) {
       f32x16 s[NA], dp[NA];
@@ -281,8 +286,9 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
       // Masked tiles only, as wave-uniform branches (opaque() on the bound keeps
       // the compiler from flattening them into selects run on every tile).
       // Element (a, v) is query q0 + 4h + r with r = 32a + 8(v/4) + v%4.
-      if (P.causal && q0 < kw + 31) {  // causal diagonal: keep query >= key
-        int lo = key - q0 - 4 * hf;
+      const int off = kb.nk - kb.nq;  // the diagonal of query i is key i + off
+      if (P.causal && q0 < kw + 31 - off) {  // causal diagonal: keep query >= key - off
+        int lo = key - off - q0 - 4 * hf;
         opaque(lo);
 #pragma unroll
         for (int a = 0; a < NA; ++a)
@@ -298,6 +304,15 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
 #pragma unroll
           for (int v = 0; v < 16; ++v)
             if (32 * a + 8 * (v >> 2) + (v & 3) >= hi) s[a][v] = 0.f;
+      }
+      if (kb.window >= 0 && q0 + BQ - 1 > kw - off + kb.window) {  // window: keep query <= key - off + window
+        int hw = key - off + kb.window - q0 - 4 * hf;
+        opaque(hw);
+#pragma unroll
+        for (int a = 0; a < NA; ++a)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (32 * a + 8 * (v >> 2) + (v & 3) > hw) s[a][v] = 0.f;
       }
       // dS = P (dP - D); both to bf16 pieces
 #pragma unroll
@@ -373,12 +388,12 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
     hg = nhg;
     it = nit;
   };
-  while (hg < group) {
+  while (qt0 < nq && hg < group) {
     tile(smem, smem + C::STAGE, ds_lds, kt_lds);
     if (hg < group) tile(smem + C::STAGE, smem, ds_lds, kt_lds);
   }
 
-  if (key < N) {
+  if (key < P.Nk) {
     __bf16* dk = reinterpret_cast<__bf16*>(P.dk) + head + (size_t)key * D;
     __bf16* dv = reinterpret_cast<__bf16*>(P.dv) + head + (size_t)key * D;
 #pragma unroll
@@ -432,12 +447,13 @@ bwd_dq_kernel(BwdParams P, int n_qtiles) {
   const int qw = q0 + 32 * wave;
   const int qrow = qw + li;
 
+  const KeyBounds kb{N, P.Nk, P.causal, P.window};
   const size_t head = (size_t)bh * N * D;
-  const size_t kvhead = (size_t)kv_head(bh, P.hq, P.group) * N * D;
-  const uint32_t head_bytes = (uint32_t)((size_t)N * D * 2);
+  const size_t kvhead = (size_t)kv_head(bh, P.hq, P.group) * P.Nk * D;
+  const uint32_t head_bytes = (uint32_t)((size_t)N * D * 2), kv_bytes = (uint32_t)((size_t)P.Nk * D * 2);
   const auto rq = make_rsrc(reinterpret_cast<const __bf16*>(P.q) + head, head_bytes);
-  const auto rk = make_rsrc(reinterpret_cast<const __bf16*>(P.k) + kvhead, head_bytes);
-  const auto rv = make_rsrc(reinterpret_cast<const __bf16*>(P.v) + kvhead, head_bytes);
+  const auto rk = make_rsrc(reinterpret_cast<const __bf16*>(P.k) + kvhead, kv_bytes);
+  const auto rv = make_rsrc(reinterpret_cast<const __bf16*>(P.v) + kvhead, kv_bytes);
   const auto rdo = make_rsrc(reinterpret_cast<const __bf16*>(P.dO) + head, head_bytes);
 
   i32x4 qf[NP], dof[NP];
@@ -478,23 +494,24 @@ bwd_dq_kernel(BwdParams P, int n_qtiles) {
 #pragma unroll
   for (int e = 0; e < NE; ++e) acc[e] = f32x16{};
 
-  const int kv_end = P.causal ? min(N, q0 + C::BM) : N;
-  const int n_tiles = (kv_end + BN - 1) / BN;
+  // key tiles [t_lo, t_end) hold every key a row of this workgroup keeps
+  const int t_lo = kb.lo(q0) / BN;
+  const int t_end = kb.hi(min(q0 + C::BM, N) - 1) / BN + 1;
 
-  issue(0, smem);
+  issue(t_lo * BN, smem);
   wait_vmem();
   __syncthreads();
 
   // One key tile; see the key-tile pass for the restrict qualifiers.
   auto tile = [&](int t, const char* __restrict__ cur, char* __restrict__ nxt) {
     const int key0 = t * BN;
-    const bool more = t + 1 < n_tiles;
+    const bool more = t + 1 < t_end;
     if (more) issue(key0 + BN, nxt);
     const char* ks = cur;
     const char* vs = ks + C::TILE;
     opaque(kbase);
     opaque(tbase);
-    if (!P.causal || key0 <= qw + 31) {
+    if (key0 <= kb.hi(qw + 31) && key0 + BN - 1 >= kb.lo(qw)) {
       // S^T = K Q^T and dP^T - D = V dO^T - D, K/V pieces read one piece ahead.
       f32x16 s[NB], dp[NB];
 #pragma unroll
@@ -531,18 +548,21 @@ bwd_dq_kernel(BwdParams P, int n_qtiles) {
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int v = 0; v < 16; ++v) s[b][v] = fast_exp2(__builtin_fmaf(s[b][v], sl2, -lse_l2));
-      // Masked tiles (causal diagonal, ragged tail) only, as a wave-uniform
-      // branch (see the key-tile pass). Element (b, v) is key key0 + 4h + r
-      // with r = 32b + 8(v/4) + v%4, kept iff the key is <= min(qrow, N-1)
-      // (causal) or <= N-1.
-      if ((key0 + BN > N) || (P.causal && key0 + BN - 1 > qw)) {
-        int lim = (P.causal ? min(qrow, N - 1) : N - 1) - key0 - 4 * hf;
-        opaque(lim);
+      // Masked tiles (causal diagonal, window start, ragged tail) only, as a
+      // wave-uniform branch (see the key-tile pass). Element (b, v) is key
+      // key0 + 4h + r with r = 32b + 8(v/4) + v%4, kept iff
+      // key_lo(qrow) <= key <= key_hi(qrow).
+      if ((key0 + BN > kb.nk) || (P.causal && key0 + BN - 1 > kb.hi(qw)) || (kb.window >= 0 && key0 < kb.lo(qw + 31))) {
+        int hi = kb.hi(qrow) - key0 - 4 * hf, lo = kb.lo(qrow) - key0 - 4 * hf;
+        opaque(hi);
+        opaque(lo);
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
-          for (int v = 0; v < 16; ++v)
-            if (32 * b + 8 * (v >> 2) + (v & 3) > lim) s[b][v] = 0.f;
+          for (int v = 0; v < 16; ++v) {
+            const int r = 32 * b + 8 * (v >> 2) + (v & 3);
+            if (r > hi || r < lo) s[b][v] = 0.f;
+          }
       }
       // dS^T = P^T (dP^T - D) as bf16 pieces of 16 keys
       bf16x8 db[BN / 16];
@@ -576,9 +596,9 @@ bwd_dq_kernel(BwdParams P, int n_qtiles) {
     if (more) wait_vmem();
     __syncthreads();
   };
-  for (int t = 0; t < n_tiles; t += 2) {
+  for (int t = t_lo; t < t_end; t += 2) {
     tile(t, smem, smem + C::STAGE);
-    if (t + 1 < n_tiles) tile(t + 1, smem + C::STAGE, smem);
+    if (t + 1 < t_end) tile(t + 1, smem + C::STAGE, smem);
   }
 
   if (qrow < N) {
@@ -611,7 +631,7 @@ static hipError_t launch_bwd(int variant, const BwdParams& p, int B, int H, hipS
   hipError_t e = launch_pre<KCD::D>(p, rows, st);
   if (e != hipSuccess) return e;
   if (variant == 0) {
-    const int nk = (p.N + KCA::BK - 1) / KCA::BK;
+    const int nk = (p.Nk + KCA::BK - 1) / KCA::BK;
     const long long gk = (long long)nk * B * HKV;
     if (gk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((bwd_dkdv_kernel<KCA, true>), dim3((unsigned)gk), dim3(KCA::NT), 0, st, p, nk);
@@ -621,7 +641,7 @@ static hipError_t launch_bwd(int variant, const BwdParams& p, int B, int H, hipS
                        reinterpret_cast<__bf16*>(p.dq), n8);
     return hipGetLastError();
   }
-  const int nk = (p.N + KCD::BK - 1) / KCD::BK;
+  const int nk = (p.Nk + KCD::BK - 1) / KCD::BK;
   const long long gk = (long long)nk * B * HKV;
   if (gk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((bwd_dkdv_kernel<KCD, false>), dim3((unsigned)gk), dim3(KCD::NT), 0, st, p, nk);

@@ -214,6 +214,21 @@ __device__ __forceinline__ int kv_head(int bh, int hq, int group) {
   return (bh / hq) * (hq / group) + (bh % hq) / group;
 }
 
+// Keys that query row i keeps: key_lo(i) <= j <= key_hi(i). The causal
+// diagonal of row i is key i + (nk - nq), so the last query row lines up with
+// the last key (bottom-right alignment); a left window w >= 0 keeps only keys
+// from i + (nk - nq) - w on. Both bounds are non-decreasing in i. Query rows
+// past the end of a head get the bounds of the same formulas (their results
+// are never stored). key_lo may exceed key_hi only for such rows.
+struct KeyBounds {
+  int nq, nk, causal, window;
+  __device__ __forceinline__ int lo(int i) const { return window >= 0 ? max(0, i + nk - nq - window) : 0; }
+  __device__ __forceinline__ int hi(int i) const { return causal ? min(nk - 1, i + nk - nq) : nk - 1; }
+  // Queries that key row j is kept by: qlo(j) <= i <= qhi(j).
+  __device__ __forceinline__ int qlo(int j) const { return causal ? max(0, j - (nk - nq)) : 0; }
+  __device__ __forceinline__ int qhi(int j) const { return window >= 0 ? min(nq - 1, j - (nk - nq) + window) : nq - 1; }
+};
+
 // vmcnt(0): all of this wave's vector-memory operations (incl. LDS DMA) done.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 

@@ -75,15 +75,15 @@ fwd_kernel(FwdParams P) {
   const int qw = q0 + 32 * wave;
   const int qrow = qw + li;
 
-  const size_t head_elems = (size_t)N * D;
-  const uint32_t head_bytes = (uint32_t)(head_elems * C::ESZ);
+  const KeyBounds kb{N, P.Nk, P.causal, P.window};
+  const size_t head_elems = (size_t)N * D, kv_elems = (size_t)P.Nk * D;
   const char* qh = reinterpret_cast<const char*>(P.q) + (size_t)bh * head_elems * C::ESZ;
   const int kvh = kv_head(bh, P.hq, P.group);
-  const char* kh = reinterpret_cast<const char*>(P.k) + (size_t)kvh * head_elems * C::ESZ;
-  const char* vh = reinterpret_cast<const char*>(P.v) + (size_t)kvh * head_elems * C::ESZ;
-  const auto rq = make_rsrc(qh, head_bytes);
-  const auto rk = make_rsrc(kh, head_bytes);
-  const auto rv = make_rsrc(vh, head_bytes);
+  const char* kh = reinterpret_cast<const char*>(P.k) + (size_t)kvh * kv_elems * C::ESZ;
+  const char* vh = reinterpret_cast<const char*>(P.v) + (size_t)kvh * kv_elems * C::ESZ;
+  const auto rq = make_rsrc(qh, (uint32_t)(head_elems * C::ESZ));
+  const auto rk = make_rsrc(kh, (uint32_t)(kv_elems * C::ESZ));
+  const auto rv = make_rsrc(vh, (uint32_t)(kv_elems * C::ESZ));
   float sc = P.scale_log2;
   float tau = P.rescale_log2;
   float out_mul = 1.f;
@@ -106,13 +106,13 @@ fwd_kernel(FwdParams P) {
     tile_pos<RB>((wave * C::LPW + i) * 64 + lane, row, ch);
     goff[i] = (uint32_t)(row * RB + ch * 16);
   }
-  auto issue = [&](int key0, char* kb) {
+  auto issue = [&](int key0, char* dst) {
     const uint32_t base = (uint32_t)key0 * RB;
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i) {
       const int m = wave * C::LPW + i;
-      buf_load_lds16(rk, goff[i] + base, 0, (lds_void*)(kb + m * 1024));
-      buf_load_lds16(rv, goff[i] + base, 0, (lds_void*)(kb + C::TILE + m * 1024));
+      buf_load_lds16(rk, goff[i] + base, 0, (lds_void*)(dst + m * 1024));
+      buf_load_lds16(rv, goff[i] + base, 0, (lds_void*)(dst + C::TILE + m * 1024));
     }
   };
 
@@ -142,10 +142,13 @@ fwd_kernel(FwdParams P) {
   for (int e = 0; e < NE; ++e) acc[e] = f32x16{};
   float m_ref = -INFINITY, l_part = 0.f;
 
-  const int kv_end = P.causal ? min(N, q0 + C::BM) : N;
-  const int n_tiles = (kv_end + BN - 1) / BN;
+  // key tiles [t_lo, t_end) hold every key a row of this workgroup keeps;
+  // this wave's rows keep none past tile w_end
+  const int t_lo = kb.lo(q0) / BN;
+  const int t_end = kb.hi(min(q0 + C::BM, N) - 1) / BN + 1;
+  const int w_end = min(t_end, kb.hi(qw + 31) / BN + 1);
 
-  issue(0, smem);
+  issue(t_lo * BN, smem);
   wait_vmem();
   __syncthreads();
 
@@ -156,11 +159,11 @@ fwd_kernel(FwdParams P) {
   // waited for explicitly (vmcnt + barrier) at the end of the tile.
   auto tile = [&](int t, const char* __restrict__ cur, char* __restrict__ nxt) {
     const int key0 = t * BN;
-    const bool more = (t + 1) < n_tiles;
+    const bool more = (t + 1) < t_end;
     if (more) issue(key0 + BN, nxt);
     const char* ks = cur;
     const char* vs = cur + C::TILE;
-    if (!P.causal || key0 <= qw + 31) {
+    if (t < w_end) {
       // ---- S^T = K Q^T ----
       // K operands are read KLA pieces ahead into a register ring: the reads
       // for piece p+KLA are issued before the MFMAs of piece p (scheduling
@@ -210,16 +213,18 @@ fwd_kernel(FwdParams P) {
           }
         }
       }
-      // ---- mask (causal diagonal / ragged tail) and tile row max ----
-      if ((key0 + BN > N) || (P.causal && key0 + BN - 1 > qw)) {
-        // key index key0 + 32b + 8(v/4) + 4h + v%4 is kept iff <= min(qrow, N-1) (causal)
-        // or <= N-1; compare the lane-independent part against one per-lane limit.
-        const int lim = (P.causal ? min(qrow, N - 1) : N - 1) - key0 - 4 * hf;
+      // ---- mask (causal diagonal, window start, ragged tail) and tile row max ----
+      if ((key0 + BN > kb.nk) || (P.causal && key0 + BN - 1 > kb.hi(qw)) || (kb.window >= 0 && key0 < kb.lo(qw + 31))) {
+        // key key0 + 32b + 8(v/4) + 4h + v%4 is kept iff key_lo(qrow) <= key <= key_hi(qrow);
+        // compare the lane-independent part r against two per-lane limits.
+        const int hi = kb.hi(qrow) - key0 - 4 * hf, lo = kb.lo(qrow) - key0 - 4 * hf;
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
-          for (int v = 0; v < 16; ++v)
-            if (32 * b + (v >> 2) * 8 + (v & 3) > lim) s[b][v] = -INFINITY;
+          for (int v = 0; v < 16; ++v) {
+            const int r = 32 * b + (v >> 2) * 8 + (v & 3);
+            if (r > hi || r < lo) s[b][v] = -INFINITY;
+          }
       }
       // row max: two chains of three-way maxima (each step folds two scores into
       // the running value, which maps to one max3), then the partner lane
@@ -236,13 +241,15 @@ fwd_kernel(FwdParams P) {
       const bool grow = mx > m_ref + tau;
       if (wave_any(grow)) {
         const float m_new = grow ? mx : m_ref;
-        const float alpha = fast_exp2(m_ref - m_new);
+        // rows that do not grow keep their scale (also when m_ref is still -inf: -inf - -inf is NaN)
+        const float alpha = grow ? fast_exp2(m_ref - m_new) : 1.f;
         m_ref = m_new;
         l_part *= alpha;
 #pragma unroll
         for (int e = 0; e < NE; ++e) acc[e] *= alpha;
       }
-      const float neg_m = -m_ref;
+      // a row that has kept no key yet (m_ref = -inf, only under a window) gets p = 2^-inf = 0
+      const float neg_m = m_ref == -INFINITY ? 0.f : -m_ref;
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -319,9 +326,9 @@ fwd_kernel(FwdParams P) {
     if (more) wait_vmem();
     __syncthreads();
   };
-  for (int t = 0; t < n_tiles; t += 2) {
+  for (int t = t_lo; t < t_end; t += 2) {
     tile(t, smem, smem + C::STAGE);
-    if (t + 1 < n_tiles) tile(t + 1, smem + C::STAGE, smem);
+    if (t + 1 < t_end) tile(t + 1, smem + C::STAGE, smem);
   }
 
   // ---- epilogue: O = acc / l, lse = ln(sum exp(s)) ----
@@ -385,12 +392,13 @@ fwd_pipe_kernel(FwdParams P) {
   const int qw = q0 + 32 * wave;
   const int qrow = qw + li;
 
-  const size_t head_elems = (size_t)N * D;
-  const uint32_t head_bytes = (uint32_t)(head_elems * 2);
-  const auto rq = make_rsrc(reinterpret_cast<const char*>(P.q) + (size_t)bh * head_elems * 2, head_bytes);
+  const KeyBounds kb{N, P.Nk, P.causal, P.window};
+  const size_t head_elems = (size_t)N * D, kv_elems = (size_t)P.Nk * D;
+  const auto rq = make_rsrc(reinterpret_cast<const char*>(P.q) + (size_t)bh * head_elems * 2,
+                            (uint32_t)(head_elems * 2));
   const int kvh = kv_head(bh, P.hq, P.group);
-  const auto rk = make_rsrc(reinterpret_cast<const char*>(P.k) + (size_t)kvh * head_elems * 2, head_bytes);
-  const auto rv = make_rsrc(reinterpret_cast<const char*>(P.v) + (size_t)kvh * head_elems * 2, head_bytes);
+  const auto rk = make_rsrc(reinterpret_cast<const char*>(P.k) + (size_t)kvh * kv_elems * 2, (uint32_t)(kv_elems * 2));
+  const auto rv = make_rsrc(reinterpret_cast<const char*>(P.v) + (size_t)kvh * kv_elems * 2, (uint32_t)(kv_elems * 2));
   const float sc = P.scale_log2;
   const float tau = P.rescale_log2;
 
@@ -401,8 +409,16 @@ fwd_pipe_kernel(FwdParams P) {
     tile_pos<RB>((wave * C::LPW + i) * 64 + lane, row, ch);
     goff[i] = (uint32_t)(row * RB + ch * 16);
   }
+  // Key tiles t_lo + j, j = 0 .. n_tiles-1, cover the keys any row of the
+  // workgroup keeps; t counts from t_lo below.
+  const int t_lo = kb.lo(q0) / BN;
+  const int n_tiles = kb.hi(min(q0 + C::BM, N) - 1) / BN + 1 - t_lo;
+  // tiles [0, n_live) hold keys this wave's queries may keep (every wave starts at t_lo: rows
+  // whose window starts later see fully masked tiles first, which add nothing)
+  const int n_live = min(n_tiles, kb.hi(qw + 31) / BN + 1 - t_lo);
+
   auto issue = [&](const __amdgpu_buffer_rsrc_t& r, int t, char* dst) {
-    const uint32_t base = (uint32_t)(t * BN) * RB;
+    const uint32_t base = (uint32_t)((t_lo + t) * BN) * RB;
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i)
       buf_load_lds16(r, goff[i] + base, 0, (lds_void*)(dst + (wave * C::LPW + i) * 1024));
@@ -421,10 +437,6 @@ fwd_pipe_kernel(FwdParams P) {
   for (int e = 0; e < NE; ++e) acc[e] = f32x16{};
   float m_ref = -INFINITY, l_part = 0.f;
 
-  const int kv_end = P.causal ? min(N, q0 + C::BM) : N;
-  const int n_tiles = (kv_end + BN - 1) / BN;
-  // key tiles holding at least one key this wave's queries may see
-  const int n_live = P.causal ? min(n_tiles, (qw + 31) / BN + 1) : n_tiles;
 
   char* const kb0 = smem;
   char* const kb1 = smem + TILE;
@@ -459,7 +471,8 @@ fwd_pipe_kernel(FwdParams P) {
   // with_s: compute scores of tile t from kt into sn; with_p: turn sp into P.
   auto scores_and_p = [&](const bool with_s, const bool with_p, const char* __restrict__ kt, f32x16 (&sn)[NB],
                           f32x16 (&sp)[NB]) __attribute__((always_inline)) {
-    const float neg_m = -m_ref;
+    // a row that has kept no key yet (m_ref = -inf, only under a window) gets p = 2^-inf = 0
+    const float neg_m = m_ref == -INFINITY ? 0.f : -m_ref;
     l4[0] = l4[1] = l4[2] = l4[3] = 0.f;
     if (with_s) {
       constexpr int KLA = 2;
@@ -502,15 +515,19 @@ fwd_pipe_kernel(FwdParams P) {
   auto pv_and_max = [&](const bool with_pv, const bool with_max, const char* __restrict__ vt, int t,
                         f32x16 (&s)[NB], bool use_max) __attribute__((always_inline)) {
     if (with_max && use_max) {
-      const int key0 = t * BN;
-      if ((key0 + BN > N) || (P.causal && key0 + BN - 1 > qw)) {
-        int lim = (P.causal ? min(qrow, N - 1) : N - 1) - key0 - 4 * hf;
-        opaque(lim);
+      // key key0 + 4h + r of tile t (r = 32b + 8(v/4) + v%4) is kept iff lo <= r <= hi
+      const int key0 = (t_lo + t) * BN;
+      if ((key0 + BN > kb.nk) || (P.causal && key0 + BN - 1 > kb.hi(qw)) || (kb.window >= 0 && key0 < kb.lo(qw + 31))) {
+        int hi = kb.hi(qrow) - key0 - 4 * hf, lo = kb.lo(qrow) - key0 - 4 * hf;
+        opaque(hi);
+        opaque(lo);
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
-          for (int v = 0; v < 16; ++v)
-            if (32 * b + (v >> 2) * 8 + (v & 3) > lim) s[b][v] = -INFINITY;
+          for (int v = 0; v < 16; ++v) {
+            const int r = 32 * b + (v >> 2) * 8 + (v & 3);
+            if (r > hi || r < lo) s[b][v] = -INFINITY;
+          }
       }
     }
     float m2[2] = {-INFINITY, -INFINITY};
@@ -551,7 +568,8 @@ fwd_pipe_kernel(FwdParams P) {
       const bool grow = mx > m_ref + tau;
       if (use_max && wave_any(grow)) {
         const float m_new = grow ? mx : m_ref;
-        const float alpha = fast_exp2(m_ref - m_new);
+        // rows that do not grow keep their scale (also when m_ref is still -inf: -inf - -inf is NaN)
+        const float alpha = grow ? fast_exp2(m_ref - m_new) : 1.f;
         m_ref = m_new;
         l_part *= alpha;
 #pragma unroll

@@ -17,8 +17,10 @@ struct FwdParams {
   const float* q_descale;  // fp8 only; nullptr means 1
   const float* k_descale;
   const float* v_descale;
-  int N;
-  int causal;
+  int N;               // query rows per head
+  int Nk;              // key rows per head
+  int causal;          // keep key j for query i only if j <= i + Nk - N (bottom-right diagonal)
+  int window;          // >= 0: also only if j >= i + Nk - N - window; < 0: no window
   int hq;              // query heads per batch entry
   int group;           // query heads per K/V head (1: one K/V head per query head)
   int n_qtiles;        // set by the launcher
@@ -43,8 +45,10 @@ struct BwdParams {
   float* ld;        // workspace: [B*H*N] lse * log2(e), then [B*H*N] -rowsum(dO * O) (H query heads)
   long long rows;   // B * H * N
   float* dq_accum;  // [B,H,N,D] float workspace (atomic variant), else nullptr
-  int N;
-  int causal;
+  int N;             // query rows per head
+  int Nk;            // key rows per head
+  int causal;        // as in FwdParams
+  int window;        // as in FwdParams
   int hq;            // query heads per batch entry (H above)
   int group;         // query heads per K/V head
   float scale;       // softmax scale

@@ -21,8 +21,9 @@ FA_F32, FA_BF16, FA_FP8_E4M3 = 0, 1, 2
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, 1, 2, 3, 4
 FA_BWD_ATOMIC, FA_BWD_DETERMINISTIC = 0, 1
 
-EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_ex", "fa_fwd_fp8", "fa_quantize_fp8", "fa_bwd_workspace_size", "fa_bwd",
-            "fa_bwd_gqa", "fa_bwd_dkdv", "fa_status_string", "fa_last_error")
+EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_general", "fa_fwd_ex", "fa_fwd_fp8", "fa_quantize_fp8",
+            "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_gqa", "fa_bwd_general", "fa_bwd_dkdv", "fa_status_string",
+            "fa_last_error")
 
 
 class FAError(RuntimeError):
@@ -44,6 +45,7 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         L.fa_fwd.argtypes = [_vp] * 5 + [_i] * 5 + [_f, _i, _vp]
         L.fa_fwd_gqa.argtypes = [_vp] * 5 + [_i] * 6 + [_f, _i, _vp]
+        L.fa_fwd_general.argtypes = [_vp] * 5 + [_i] * 8 + [_f, _i, _vp]
         L.fa_fwd_ex.argtypes = [_vp] * 5 + [_i] * 5 + [_f, _i, _f, _vp]
         L.fa_fwd_fp8.argtypes = [_vp] * 5 + [_i] * 5 + [_f] + [_vp] * 3 + [_vp]
         L.fa_quantize_fp8.argtypes = [_vp, _sz, _vp, _vp, _vp]
@@ -51,13 +53,14 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd_workspace_size.restype = _sz
         L.fa_bwd.argtypes = [_vp] * 9 + [_i] * 5 + [_f, _i, _i, _vp, _sz, _vp]
         L.fa_bwd_gqa.argtypes = [_vp] * 9 + [_i] * 6 + [_f, _i, _i, _vp, _sz, _vp]
+        L.fa_bwd_general.argtypes = [_vp] * 9 + [_i] * 8 + [_f, _i, _i, _vp, _sz, _vp]
         L.fa_bwd_dkdv.argtypes = [_vp] * 8 + [_i] * 5 + [_f, _i, _vp, _sz, _vp]
         L.fa_status_string.argtypes = [_i]
         L.fa_status_string.restype = ctypes.c_char_p
         L.fa_last_error.argtypes = []
         L.fa_last_error.restype = ctypes.c_char_p
-        for name in ("fa_fwd", "fa_fwd_gqa", "fa_fwd_ex", "fa_fwd_fp8", "fa_quantize_fp8", "fa_bwd", "fa_bwd_gqa",
-                     "fa_bwd_dkdv"):
+        for name in ("fa_fwd", "fa_fwd_gqa", "fa_fwd_general", "fa_fwd_ex", "fa_fwd_fp8", "fa_quantize_fp8", "fa_bwd",
+                     "fa_bwd_gqa", "fa_bwd_general", "fa_bwd_dkdv"):
             getattr(L, name).restype = _i
         _lib = L
     return _lib
@@ -90,8 +93,9 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def _check_qkv(*ts: torch.Tensor, kv=()):
-    """q-shaped tensors `ts` and K/V-shaped tensors `kv` (same B, N, D; H a multiple of their head count)."""
+def _check_qkv(*ts: torch.Tensor, kv=(), same_len=True):
+    """q-shaped tensors `ts` and K/V-shaped tensors `kv` (same B and D, H a multiple of their head count,
+    and the same length unless `same_len` is False)."""
     ref = ts[0]
     if ref.dim() != 4:
         raise ValueError("tensors must be [B, H, N, D]")
@@ -111,23 +115,36 @@ def _check_qkv(*ts: torch.Tensor, kv=()):
             if t.dim() != 4 or t.shape != k0.shape:
                 raise ValueError("k and v must share one shape")
         B, H, N, D = ref.shape
-        if k0.shape[0] != B or k0.shape[2] != N or k0.shape[3] != D or k0.shape[1] < 1 or H % k0.shape[1]:
-            raise ValueError("k/v must be [B, Hkv, N, D] with Hkv dividing the query heads")
+        if k0.shape[0] != B or k0.shape[3] != D or k0.shape[1] < 1 or H % k0.shape[1]:
+            raise ValueError("k/v must be [B, Hkv, Nk, D] with Hkv dividing the query heads")
+        if same_len and k0.shape[2] != N:
+            raise ValueError("k/v must have as many rows as q here")
 
 
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False, scale: Optional[float] = None,
         rescale_log2: Optional[float] = None, out: Optional[torch.Tensor] = None,
-        lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Attention forward. Returns (O, lse); O is float32 for float32 inputs, bf16 otherwise."""
-    _check_qkv(q, kv=(k, v))
+        lse: Optional[torch.Tensor] = None, window: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Attention forward. Returns (O, lse); O is float32 for float32 inputs, bf16 otherwise.
+
+    k, v may have fewer heads (grouped-query) and a different length than q (causal is then
+    aligned at the bottom right); `window` (>= 0) keeps only the keys from i + Nk - Nq - window on.
+    """
+    _check_qkv(q, kv=(k, v), same_len=False)
     B, H, N, D = q.shape
-    Hkv = k.shape[1]
+    Hkv, Nk = k.shape[1], k.shape[2]
     code = _dtype_code(q)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32 if code == FA_F32 else torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if Nk != N or window is not None:
+        if rescale_log2 is not None:
+            raise ValueError("rescale_log2 is only taken with equal lengths and no window")
+        _check(lib().fa_fwd_general(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,
+                                    Hkv, N, Nk, D, int(causal), -1 if window is None else int(window), scale, code,
+                                    _stream(q)))
+        return out, lse
     if Hkv != H:
         if rescale_log2 is not None:
             raise ValueError("rescale_log2 is only taken with as many K/V heads as query heads")
@@ -183,11 +200,11 @@ def bwd_workspace_size(B: int, H: int, N: int, D: int, variant: int = FA_BWD_ATO
 
 
 def bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None, variant: int = FA_BWD_ATOMIC,
-        workspace: Optional[torch.Tensor] = None, dq=None, dk=None, dv=None):
+        workspace: Optional[torch.Tensor] = None, dq=None, dk=None, dv=None, window: Optional[int] = None):
     """Attention backward (bf16). Returns (dQ, dK, dV) as bf16 tensors; dK, dV have k's shape."""
-    _check_qkv(q, o, do, kv=(k, v))
+    _check_qkv(q, o, do, kv=(k, v), same_len=False)
     B, H, N, D = q.shape
-    Hkv = k.shape[1]
+    Hkv, Nk = k.shape[1], k.shape[2]
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if lse.dtype != torch.float32 or lse.shape != (B, H, N) or not lse.is_contiguous():
         raise ValueError("lse must be contiguous float32 [B, H, N]")
@@ -197,6 +214,12 @@ def bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    if Nk != N or window is not None:
+        _check(lib().fa_bwd_general(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                    lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, Nk, D,
+                                    int(causal), -1 if window is None else int(window), scale, _dtype_code(q),
+                                    variant, workspace.data_ptr(), workspace.numel(), _stream(q)))
+        return dq, dk, dv
     if Hkv != H:
         _check(lib().fa_bwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
                                 lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, D,

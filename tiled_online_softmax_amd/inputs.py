@@ -38,6 +38,8 @@ class Workload:
     multiplier: float = 1.0
     seed: int = SEED_BASE
     hkv: Optional[int] = None  # K/V heads (grouped-query attention); None means H
+    nk: Optional[int] = None   # key length; None means N (causal is aligned at the bottom right)
+    window: Optional[int] = None  # left window; None means none
 
     @property
     def scale(self) -> float:
@@ -49,17 +51,27 @@ class Workload:
 
     @property
     def kv_shape(self):
-        return (self.B, self.H if self.hkv is None else self.hkv, self.N, self.D)
+        return (self.B, self.H if self.hkv is None else self.hkv, self.N if self.nk is None else self.nk, self.D)
+
+    def pairs(self) -> float:
+        """(query, key) pairs one head computes: N^2, halved for causal with equal lengths and no window;
+        otherwise the exact count of kept pairs."""
+        nk = self.N if self.nk is None else self.nk
+        if self.window is None and (not self.causal or nk == self.N):
+            return self.N * nk / 2.0 if self.causal else float(self.N * nk)
+        i = np.arange(self.N, dtype=np.int64)
+        off = nk - self.N
+        lo = np.maximum(0, i + off - self.window) if self.window is not None else np.zeros_like(i)
+        hi = np.minimum(nk - 1, i + off) if self.causal else np.full_like(i, nk - 1)
+        return float(np.maximum(0, hi - lo + 1).sum())
 
     def fwd_flops(self) -> float:
-        """Two N x N x D contractions (QK^T and PV), 2 flops per FMA; causal is half."""
-        f = 4.0 * self.B * self.H * self.N * self.N * self.D
-        return f / 2 if self.causal else f
+        """Two contractions (QK^T and PV) over the kept pairs, D multiply-adds each, 2 flops per FMA."""
+        return 4.0 * self.B * self.H * self.pairs() * self.D
 
     def bwd_flops(self) -> float:
-        """Five N x N x D contractions (S, dV, dP, dQ, dK); causal is half."""
-        f = 10.0 * self.B * self.H * self.N * self.N * self.D
-        return f / 2 if self.causal else f
+        """Five contractions (S, dV, dP, dQ, dK) over the kept pairs."""
+        return 10.0 * self.B * self.H * self.pairs() * self.D
 
 
 # The five workloads the library is specified and measured on.
@@ -72,6 +84,10 @@ WORKLOADS: Dict[str, Workload] = {
     # Grouped-query attention (a NEXT-row extension): 32 query heads sharing 8 K/V heads.
     "gqa_causal_bf16": Workload("gqa_causal_bf16", 4, 32, 2048, 128, "bf16", True, "fwd+bwd", seed=SEED_BASE + 6,
                                 hkv=8),
+    # Queries extending a cached prefix (1024 new rows after 3072 cached keys), causal at the bottom right.
+    "prefill_bf16": Workload("prefill_bf16", 4, 16, 1024, 128, "bf16", True, "fwd+bwd", seed=SEED_BASE + 7, nk=4096),
+    # Sliding window: every row keeps the 1024 keys ending at its diagonal.
+    "swa_bf16": Workload("swa_bf16", 2, 16, 8192, 128, "bf16", True, "fwd+bwd", seed=SEED_BASE + 8, window=1023),
 }
 
 
