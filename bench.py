@@ -152,16 +152,16 @@ def breakdown():
             fn = lambda: fa.fwd_fp8(qc, kc, vc, causal=w.causal, q_descale=qd, k_descale=kd, v_descale=vd)
             legs.append((name, "fwd", fn, w.fwd_flops(), PEAK_TFLOPS["fp8"], 10))
         if w.passes in ("fwd", "fwd+bwd") and w.dtype != "fp8":
-            fn = lambda: fa.fwd(x["q"], x["k"], x["v"], causal=w.causal)
+            fn = lambda: fa.fwd(x["q"], x["k"], x["v"], causal=w.causal, window=w.window)
             peak = PEAK_TFLOPS["f32" if w.dtype == "f32" else "bf16"]
             legs.append((name if w.passes == "fwd" else name + ":fwd", "fwd", fn, w.fwd_flops(), peak,
                          200 if w.N <= 2048 else 30))
         if w.passes in ("bwd", "fwd+bwd"):
-            o, lse = fa.fwd(x["q"], x["k"], x["v"], causal=w.causal)
+            o, lse = fa.fwd(x["q"], x["k"], x["v"], causal=w.causal, window=w.window)
             ws = torch.empty(fa.bwd_workspace_size(w.B, w.H, w.N, w.D, fa.FA_BWD_DETERMINISTIC), dtype=torch.uint8,
                              device="cuda:0")
             fn = lambda: fa.bwd(x["q"], x["k"], x["v"], o, x["do"], lse, causal=w.causal,
-                                variant=fa.FA_BWD_DETERMINISTIC, workspace=ws)
+                                variant=fa.FA_BWD_DETERMINISTIC, workspace=ws, window=w.window)
             legs.append((name if w.passes == "bwd" else name + ":bwd", "bwd", fn, w.bwd_flops(), PEAK_TFLOPS["bf16"],
                          50))
         for label, pss, fn, flops, peak, iters in legs:

@@ -1,7 +1,8 @@
 """Exact scaled-dot-product attention in float64 -- oracle (test infrastructure only).
 
 Conventions (the pages fix none of them; these are the plainest readings):
-  * tensors are contiguous [B, H, N, D]; queries and keys have the same length N;
+  * tensors are contiguous [B, H, N, D]: queries have N_q rows and keys N_k
+    (N_q = N_k unless a call says otherwise);
   * grouped-query attention (named on the page "FlashAttention" entity trail,
     section "Corpus findings", AVO entry): K and V may have Hkv heads with Hkv
     dividing H; query head h then uses K/V head h // (H // Hkv), i.e. each run

@@ -120,7 +120,7 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
   // walks the query tiles of every head of the group, which sums their dK and
   // dV contributions in the accumulators.
   int bh, kt;
-  wg_map(n_ktiles, P.causal, bh, kt);
+  wg_map(n_ktiles, P.causal, 1, bh, kt);
   const int N = P.N;  // query rows per head
   const KeyBounds kb{N, P.Nk, P.causal, P.window};
   const int group = P.group;
@@ -440,7 +440,7 @@ bwd_dq_kernel(BwdParams P, int n_qtiles) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps per-wave branches scalar
 
   int bh, qt;
-  wg_map(n_qtiles, P.causal, bh, qt);
+  wg_map(n_qtiles, P.causal, P.group, bh, qt);
   if (P.causal) qt = n_qtiles - 1 - qt;
   const int N = P.N;
   const int q0 = qt * C::BM;

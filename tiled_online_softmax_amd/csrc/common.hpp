@@ -190,15 +190,22 @@ __device__ __forceinline__ uint32_t tr8_off(int lane, int e) {
 // of a head cost from one to n_tiles units, and a head-by-head order leaves
 // long workgroups for the end of the launch; there the order is rank-major
 // (rank 0, the costliest tile, of every head first), which schedules the
-// longest workgroups first. When the head count is a multiple of 8, XCD x then
-// gets the contiguous heads [x*BH/8, (x+1)*BH/8), so neighbouring query heads
-// that share K/V heads share an L2.
-__device__ __forceinline__ void wg_map(int n_tiles, bool causal, int& bh, int& rank) {
+// longest workgroups first. The `group` consecutive heads that share one K/V
+// head stay on one XCD (whole groups u with u % 8 = x on XCD x) when the head
+// count is a multiple of 8 * group, so their K/V tiles are fetched into one L2.
+// (Giving each XCD a contiguous block of heads instead raised the backward
+// key-tile pass's L2 misses by about half, with no change in its time.)
+__device__ __forceinline__ void wg_map(int n_tiles, bool causal, int group, int& bh, int& rank) {
   const int G = gridDim.x, g = blockIdx.x;
   if (causal) {
     const int BH = G / n_tiles;
     const int i = g % BH;
-    bh = (BH & 7) == 0 ? (i & 7) * (BH >> 3) + (i >> 3) : i;
+    if (BH % (8 * group) == 0) {
+      const int j = i >> 3;
+      bh = ((i & 7) + 8 * (j / group)) * group + j % group;
+    } else {
+      bh = i;
+    }
     rank = g / BH;
   } else {
     const int w = (G & 7) == 0 ? (g & 7) * (G >> 3) + (g >> 3) : g;

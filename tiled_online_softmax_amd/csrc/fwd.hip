@@ -68,7 +68,7 @@ fwd_kernel(FwdParams P) {
   // Workgroup -> (head, query tile); under causal masking the last query
   // tiles carry the most key tiles, so rank 0 is the last one.
   int bh, qt;
-  wg_map(P.n_qtiles, P.causal, bh, qt);
+  wg_map(P.n_qtiles, P.causal, P.group, bh, qt);
   if (P.causal) qt = P.n_qtiles - 1 - qt;
   const int N = P.N;
   const int q0 = qt * C::BM;
@@ -385,7 +385,7 @@ fwd_pipe_kernel(FwdParams P) {
   const int li = lane & 31, hf = lane >> 5;
 
   int bh, qt;
-  wg_map(P.n_qtiles, P.causal, bh, qt);
+  wg_map(P.n_qtiles, P.causal, P.group, bh, qt);
   if (P.causal) qt = P.n_qtiles - 1 - qt;
   const int N = P.N;
   const int q0 = qt * C::BM;
