@@ -12,13 +12,22 @@ Conventions (the pages fix none of them; these are the plainest readings):
     aligned with the last key (bottom-right), as when queries extend a cached
     prefix of keys (the KV-cache prefill named in the FlashPrefill V2 entry of
     the page "FlashAttention" entity trail, section "Corpus findings"); with
-    equal lengths this is j <= i. Causal needs N_k >= N_q, so no row is empty;
+    equal lengths this is j <= i;
   * a left window w >= 0 also drops keys j < i + (N_k - N_q) - w, i.e. a row
     keeps at most the w + 1 keys ending at its diagonal (the local
     sliding-window attention of the WAND entry on the "attention mechanism"
     tag page, and the local window of the NanoGPT speedrun post on the "MHA"
     search page); w < 0 means no window;
-  * lse_i = log(sum_j exp(s_ij)) with the natural logarithm, over the kept keys.
+  * lse_i = log(sum_j exp(s_ij)) with the natural logarithm, over the kept keys;
+  * a row that keeps no key (causal with N_k < N_q leaves the first N_q - N_k
+    rows so; a packed sequence may have no keys) has an empty sum: lse_i =
+    ln 0 = -inf, and its output is taken as 0 (the sum of p_ij v_j over no
+    keys), so it does not depend on Q, K or V and its gradients are 0;
+  * packed variable-length batches (``forward_varlen`` / ``backward_varlen``)
+    are independent problems, one per sequence: rows cu[b] .. cu[b+1]-1 of the
+    packed [total, H, D] tensors are sequence b, with these conventions inside
+    each sequence (the continuous batching of the FlashPrefill V2 entry on the
+    page "FlashAttention" entity trail, section "Corpus findings").
 
 The method on the pages (tiling, online softmax, deferred normalisation,
 conditional rescaling -- page "r/mlscaling", FA1-FA4 version list) reaches this
@@ -41,11 +50,6 @@ def _row_blocks(n_rows, n_cols):
     rows = max(1, _ROW_BLOCK_BYTES // (8 * max(1, n_cols)))
     for r0 in range(0, n_rows, rows):
         yield r0, min(n_rows, r0 + rows)
-
-
-def _check_lengths(n_q, n_k, causal):
-    if causal and n_k < n_q:
-        raise ValueError(f"causal attention needs at least as many keys ({n_k}) as queries ({n_q})")
 
 
 def _group(h_q, h_kv):
@@ -83,11 +87,18 @@ def scores(q, k, scale, causal, rows=None, n_q=None, window=-1):
 
 
 def softmax_rows(s):
-    """Row softmax of a score block; returns (P, lse). Max-subtracted for range only."""
-    m = s.max(axis=1)
-    p = np.exp(s - m[:, None])
+    """Row softmax of a score block; returns (P, lse). Max-subtracted for range only.
+
+    A row whose scores are all -inf keeps no key: its P row is 0 and its lse -inf.
+    """
+    m = s.max(axis=1) if s.shape[1] else np.full(s.shape[0], -np.inf)
+    empty = m == -np.inf
+    m0 = np.where(empty, 0.0, m)
+    p = np.exp(s - m0[:, None])  # exp(-inf) = 0 on every entry of an empty row
     l = p.sum(axis=1)
-    return p / l[:, None], m + np.log(l)
+    l1 = np.where(empty, 1.0, l)
+    lse = np.where(empty, -np.inf, m0 + np.log(l1))
+    return p / l1[:, None], lse
 
 
 def forward(q, k, v, causal, scale, rows=None, window=-1):
@@ -109,7 +120,6 @@ def forward(q, k, v, causal, scale, rows=None, window=-1):
     v = _as_f64(v)
     B, H, N, D = q.shape
     G = _group(H, k.shape[1])
-    _check_lengths(N, k.shape[2], causal)
     sel = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
     M = sel.shape[0]
     o = np.empty((B, H, M, v.shape[-1]))
@@ -149,7 +159,6 @@ def backward(q, k, v, do, causal, scale, window=-1):
     dv = np.zeros_like(v)
     B, H, N, D = q.shape
     G = _group(H, k.shape[1])
-    _check_lengths(N, k.shape[2], causal)
     for b in range(B):
         for h in range(H):
             kh = h // G
@@ -160,4 +169,47 @@ def backward(q, k, v, do, causal, scale, window=-1):
             ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
             dq[b, h] = scale * (ds @ k[b, kh])
             dk[b, kh] += scale * (ds.T @ q[b, h])
+    return dq, dk, dv
+
+
+def _check_cu(cu, total, B):
+    cu = np.asarray(cu, dtype=np.int64)
+    if cu.shape != (B + 1,) or cu[0] != 0 or cu[-1] != total or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens must be [B + 1] non-decreasing offsets from 0 to the packed length")
+    return cu
+
+
+def forward_varlen(q, k, v, cu_q, cu_k, causal, scale, window=-1):
+    """Packed variable-length forward: q [T_q, H, D], k, v [T_k, Hkv, D]; sequence b is
+    rows cu_q[b] .. cu_q[b+1]-1 of q and cu_k[b] .. cu_k[b+1]-1 of k and v.
+    Returns O [T_q, H, D] and lse [H, T_q], float64."""
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    B = len(cu_q) - 1
+    cu_q, cu_k = _check_cu(cu_q, q.shape[0], B), _check_cu(cu_k, k.shape[0], B)
+    o = np.zeros((q.shape[0], q.shape[1], v.shape[2]))
+    lse = np.full((q.shape[1], q.shape[0]), -np.inf)
+    for b in range(B):
+        qs, ks = slice(cu_q[b], cu_q[b + 1]), slice(cu_k[b], cu_k[b + 1])
+        if cu_q[b + 1] == cu_q[b]:
+            continue
+        # one sequence as a [1, H, n, D] problem
+        ob, lb = forward(q[qs].transpose(1, 0, 2)[None], k[ks].transpose(1, 0, 2)[None],
+                         v[ks].transpose(1, 0, 2)[None], causal, scale, window=window)
+        o[qs] = ob[0].transpose(1, 0, 2)
+        lse[:, qs] = lb[0]
+    return o, lse
+
+
+def backward_varlen(q, k, v, do, cu_q, cu_k, causal, scale, window=-1):
+    """Gradients of the packed variable-length forward, one sequence at a time.
+    Returns dQ [T_q, H, D], dK and dV [T_k, Hkv, D], float64 (keys of no sequence get 0)."""
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    B = len(cu_q) - 1
+    cu_q, cu_k = _check_cu(cu_q, q.shape[0], B), _check_cu(cu_k, k.shape[0], B)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        qs, ks = slice(cu_q[b], cu_q[b + 1]), slice(cu_k[b], cu_k[b + 1])
+        t = lambda x, sl: x[sl].transpose(1, 0, 2)[None]
+        gq, gk, gv = backward(t(q, qs), t(k, ks), t(v, ks), t(do, qs), causal, scale, window=window)
+        dq[qs], dk[ks], dv[ks] = gq[0].transpose(1, 0, 2), gk[0].transpose(1, 0, 2), gv[0].transpose(1, 0, 2)
     return dq, dk, dv

@@ -27,6 +27,10 @@ def forward(q, k, v, causal, scale, window=-1):
     o, lse = [], []
     for i in range(n):
         keys = _keys(i, n, len(k), causal, window)
+        if not keys:  # a row that keeps no key: empty sum, lse = ln 0, output 0
+            o.append([0.0] * len(v[0]) if v else [])
+            lse.append(-math.inf)
+            continue
         s = [scale * _dot(q[i], k[j]) for j in keys]
         m = max(s)
         e = [math.exp(x - m) for x in s]
@@ -43,6 +47,9 @@ def backward(q, k, v, do, causal, scale, window=-1):
     p = []
     for i in range(n):
         kept = set(_keys(i, n, nk, causal, window))
+        if not kept:  # a row that keeps no key has P = 0 (its output is the constant 0)
+            p.append([0.0] * nk)
+            continue
         s = [(scale * _dot(q[i], k[j]) if j in kept else -math.inf) for j in range(nk)]
         m = max(s)
         e = [0.0 if x == -math.inf else math.exp(x - m) for x in s]

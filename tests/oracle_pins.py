@@ -27,7 +27,15 @@ own code:
   * grouped K/V heads: torch's scaled_dot_product_attention with enable_gqa
     and its autograd, and the identity that a group's shared K/V head gives
     the same outputs as every query head holding its own copy (whose dK and dV
-    then add up to the shared head's).
+    then add up to the shared head's);
+  * rows that keep no key (causal with fewer keys than queries, no keys at
+    all): O = 0 and lse = -inf exactly, the other rows equal torch's
+    top-left causal attention of the remaining queries, with zero gradients
+    for the empty rows and torch autograd for the rest;
+  * packed variable-length batches: torch's scaled_dot_product_attention and
+    autograd on the zero-padded batch with an explicit boolean mask built from
+    the lengths (a formulation by masking, not by slicing), including empty
+    sequences on either side.
 """
 from __future__ import annotations
 
@@ -333,7 +341,8 @@ def pin_window_equals_key_slice(fwd, tol=1e-12):
 def pin_brute_force_masks(fwd, bwd, brute, tol=1e-12):
     """The scalar-loop oracle with N_q != N_k and windows, forward and backward, on tiny heads."""
     for (Nq, Nk, causal, w, seed) in [(5, 9, True, 2, 110), (7, 7, True, 0, 111), (6, 4, False, 1, 112),
-                                       (3, 11, True, -1, 113), (8, 8, False, 3, 114)]:
+                                       (3, 11, True, -1, 113), (8, 8, False, 3, 114), (7, 3, True, -1, 115),
+                                       (6, 4, True, 1, 116)]:
         q, do = _rand((1, 1, Nq, 4), seed), _rand((1, 1, Nq, 4), seed + 3)
         k, v = _rand((1, 1, Nk, 4), seed + 1), _rand((1, 1, Nk, 4), seed + 2)
         o, lse = fwd(q, k, v, causal, 0.6, window=w)
@@ -367,3 +376,91 @@ def pin_finite_differences_masks(fwd, bwd, tol=1e-7):
 
 FORWARD_PINS = [pin_zero_query, pin_constant_scores, pin_ones_value, pin_permutation, pin_key_shift,
                 pin_scale_fold, pin_torch_forward]
+
+
+def pin_empty_rows(fwd, bwd, tol=1e-11):
+    """Causal with N_k < N_q: rows i < N_q - N_k keep no key -> O = 0, lse = -inf, zero dQ; the
+    other rows are top-left causal attention of q[N_q - N_k:] (torch sdpa is_causal, a library
+    routine). No keys at all: every row is empty."""
+    import torch
+
+    B, H, Nq, Nk, D = 1, 2, 9, 4, 8
+    q, do = _rand((B, H, Nq, D), 130), _rand((B, H, Nq, D), 133)
+    k, v = _rand((B, H, Nk, D), 131), _rand((B, H, Nk, D), 132)
+    e = Nq - Nk
+    o, lse = fwd(q, k, v, True, 0.45)
+    assert np.all(o[:, :, :e] == 0.0) and np.all(lse[:, :, :e] == -np.inf)
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_() for x in (q[:, :, e:].copy(), k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=0.45)
+    np.testing.assert_allclose(o[:, :, e:], ref.detach().numpy(), atol=tol)
+    s = 0.45 * (tq @ tk.transpose(-1, -2))
+    s = s.masked_fill(torch.ones(Nk, Nk, dtype=torch.bool).triu(1), float("-inf"))
+    np.testing.assert_allclose(lse[:, :, e:], torch.logsumexp(s, dim=-1).detach().numpy(), atol=tol)
+    ref.backward(torch.from_numpy(do[:, :, e:].copy()))
+    dq, dk, dv = bwd(q, k, v, do, True, 0.45)
+    assert np.all(dq[:, :, :e] == 0.0)
+    np.testing.assert_allclose(dq[:, :, e:], tq.grad.numpy(), atol=tol)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), atol=tol)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), atol=tol)
+    # no keys at all
+    o0, lse0 = fwd(q, k[:, :, :0], v[:, :, :0], False, 0.45)
+    assert np.all(o0 == 0.0) and np.all(lse0 == -np.inf)
+
+
+VARLEN_LENGTHS = [(5, 5), (0, 3), (7, 12), (4, 0), (1, 9), (6, 6), (9, 4)]
+
+
+def pin_varlen_padded(fwd_varlen, bwd_varlen, tol=1e-11):
+    """Packed sequences against torch sdpa + autograd on the zero-padded batch with a boolean mask
+    built from each sequence's lengths (bottom-right causal, left window), grouped K/V heads."""
+    import torch
+
+    H, Hkv, D, scale = 4, 2, 8, 0.35
+    nq = [a for a, _ in VARLEN_LENGTHS]
+    nk = [b for _, b in VARLEN_LENGTHS]
+    B, Lq, Lk = len(nq), max(nq), max(nk)
+    cu_q, cu_k = np.concatenate([[0], np.cumsum(nq)]), np.concatenate([[0], np.cumsum(nk)])
+    for causal, w, seed in [(False, -1, 140), (True, -1, 141), (True, 3, 142), (False, 2, 143)]:
+        q, do = _rand((cu_q[-1], H, D), seed), _rand((cu_q[-1], H, D), seed + 3)
+        k, v = _rand((cu_k[-1], Hkv, D), seed + 1), _rand((cu_k[-1], Hkv, D), seed + 2)
+        o, lse = fwd_varlen(q, k, v, cu_q, cu_k, causal, scale, window=w)
+        dq, dk, dv = bwd_varlen(q, k, v, do, cu_q, cu_k, causal, scale, window=w)
+        # padded batch: [B, H, L, D], mask[b, i, j] True where query i of sequence b keeps key j
+        pad = lambda x, cu, n, L, h: np.stack([np.pad(x[cu[b]:cu[b + 1]], ((0, L - n[b]), (0, 0), (0, 0)))
+                                               for b in range(B)]).transpose(0, 2, 1, 3)
+        qp, dop = pad(q, cu_q, nq, Lq, H), pad(do, cu_q, nq, Lq, H)
+        kp, vp = pad(k, cu_k, nk, Lk, Hkv), pad(v, cu_k, nk, Lk, Hkv)
+        i = np.arange(Lq)[:, None]
+        j = np.arange(Lk)[None, :]
+        mask = np.zeros((B, 1, Lq, Lk), dtype=bool)
+        for b in range(B):
+            keep = (i < nq[b]) & (j < nk[b])
+            if causal:
+                keep &= j <= i + nk[b] - nq[b]
+            if w >= 0:
+                keep &= j >= i + nk[b] - nq[b] - w
+            mask[b, 0] = keep
+        live = mask.any(axis=3)  # [B, 1, Lq]: rows that keep a key
+        safe = mask.copy()
+        safe[..., 0] |= ~live  # a dummy key for empty rows (their dO is zeroed below)
+        tq, tk, tv = (torch.from_numpy(x).requires_grad_() for x in (qp, kp, vp))
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(safe),
+                                                               scale=scale, enable_gqa=True)
+        g = H // Hkv
+        s = scale * (tq @ tk.repeat_interleave(g, dim=1).transpose(-1, -2))
+        lse_ref = torch.logsumexp(s.masked_fill(~torch.from_numpy(mask), float("-inf")), dim=-1)
+        ref.backward(torch.from_numpy(dop * live[..., None]))
+        for b in range(B):
+            rows = slice(cu_q[b], cu_q[b + 1])
+            lv = live[b, 0, :nq[b]]
+            o_b = o[rows].transpose(1, 0, 2)       # [H, n, D]
+            lse_b = lse[:, rows]
+            np.testing.assert_allclose(o_b[:, lv], ref.detach().numpy()[b][:, :nq[b]][:, lv], atol=tol)
+            np.testing.assert_allclose(lse_b[:, lv], lse_ref.detach().numpy()[b][:, :nq[b]][:, lv], atol=tol)
+            assert np.all(o_b[:, ~lv] == 0.0) and np.all(lse_b[:, ~lv] == -np.inf)
+            dq_b = dq[rows].transpose(1, 0, 2)
+            np.testing.assert_allclose(dq_b[:, lv], tq.grad.numpy()[b][:, :nq[b]][:, lv], atol=tol)
+            assert np.all(dq_b[:, ~lv] == 0.0)
+            keys = slice(cu_k[b], cu_k[b + 1])
+            np.testing.assert_allclose(dk[keys].transpose(1, 0, 2), tk.grad.numpy()[b][:, :nk[b]], atol=tol)
+            np.testing.assert_allclose(dv[keys].transpose(1, 0, 2), tv.grad.numpy()[b][:, :nk[b]], atol=tol)

@@ -61,9 +61,19 @@ def test_finite_differences_masks():
     pins.pin_finite_differences_masks(attention.forward, attention.backward)
 
 
-def test_causal_needs_enough_keys():
-    with pytest.raises(ValueError):
-        attention.forward(np.zeros((1, 1, 5, 2)), np.zeros((1, 1, 4, 2)), np.zeros((1, 1, 4, 2)), True, 1.0)
+def test_empty_rows():
+    pins.pin_empty_rows(attention.forward, attention.backward)
+
+
+def test_varlen_padded():
+    pins.pin_varlen_padded(attention.forward_varlen, attention.backward_varlen)
+
+
+def test_varlen_rejects_bad_offsets():
+    q = np.zeros((5, 1, 2))
+    for cu_k in ([0, 5], [0, 6, 5], [1, 3, 5], [0, 2, 4], [0, 3, 2, 5]):
+        with pytest.raises(ValueError):
+            attention.forward_varlen(q, q, q, [0, 2, 5], cu_k, False, 1.0)
 
 
 def test_brute_force():

@@ -237,3 +237,99 @@ def test_unmutated_mask_factory_passes():
     pins.pin_window_closed_forms(fwd)
     pins.pin_window_equals_key_slice(fwd)
     pins.pin_brute_force_masks(fwd, bwd, brute)
+
+
+def _empty_factory(nan_rows=False, lse_zero=False):
+    """The oracle with one planted mistake in rows that keep no key: the plain softmax (0/0 there),
+    or lse = 0 instead of -inf for them."""
+    def softmax(s):
+        if nan_rows:
+            with np.errstate(invalid="ignore", divide="ignore"):
+                m = s.max(axis=1)
+                p = np.exp(s - m[:, None])
+                l = p.sum(axis=1)
+                return p / l[:, None], m + np.log(l)
+        p, lse = attention.softmax_rows(s)
+        return p, (np.where(lse == -np.inf, 0.0, lse) if lse_zero else lse)
+
+    def fwd(q, k, v, causal, scale, rows=None, window=-1):
+        q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+        B, H, N, _ = q.shape
+        o, lse = np.empty((B, H, N, v.shape[-1])), np.empty((B, H, N))
+        for b in range(B):
+            for h in range(H):
+                p, lse[b, h] = softmax(attention.scores(q[b, h], k[b, h], scale, causal, window=window))
+                o[b, h] = p @ v[b, h]
+        return o, lse
+
+    def bwd(q, k, v, do, causal, scale, window=-1):
+        q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+        dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+        B, H = q.shape[:2]
+        for b in range(B):
+            for h in range(H):
+                p, _ = softmax(attention.scores(q[b, h], k[b, h], scale, causal, window=window))
+                dv[b, h] = p.T @ do[b, h]
+                dp = do[b, h] @ v[b, h].T
+                ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+                dq[b, h] = scale * (ds @ k[b, h])
+                dk[b, h] = scale * (ds.T @ q[b, h])
+        return dq, dk, dv
+    return fwd, bwd
+
+
+@pytest.mark.parametrize("mutant", ["nan_rows", "lse_zero"])
+def test_empty_row_mutants_fail_a_pin(mutant):
+    fwd, bwd = _empty_factory(nan_rows=mutant == "nan_rows", lse_zero=mutant == "lse_zero")
+    with pytest.raises((AssertionError, ValueError)):
+        pins.pin_empty_rows(fwd, bwd)
+
+
+def test_unmutated_empty_factory_passes():
+    pins.pin_empty_rows(*_empty_factory())
+
+
+def _varlen_factory(key_overrun=False, global_diagonal=False):
+    """Packed sequences through the oracle's per-head forward and backward with one planted
+    mistake: each sequence also sees the next sequence's first key, or the causal diagonal of every
+    sequence is placed from the longest lengths instead of its own."""
+    def run(q, k, v, do, cu_q, cu_k, causal, scale, window):
+        B = len(cu_q) - 1
+        nq, nk = np.diff(cu_q), np.diff(cu_k)
+        Lq, Lk = nq.max(), nk.max()
+        o, lse = np.zeros((q.shape[0], q.shape[1], v.shape[2])), np.full((q.shape[1], q.shape[0]), -np.inf)
+        dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+        G = q.shape[1] // k.shape[1]
+        for b in range(B):
+            qs = slice(cu_q[b], cu_q[b + 1])
+            ks = slice(cu_k[b], min(cu_k[b + 1] + (1 if key_overrun else 0), k.shape[0]))
+            n_q = nk[b] - (Lk - Lq) if global_diagonal else nq[b]
+            for h in range(q.shape[1]):
+                qh, kh, vh = q[qs, h], k[ks, h // G], v[ks, h // G]
+                s = attention.scores(qh, kh, scale, causal, rows=np.arange(nq[b]), n_q=n_q, window=window)
+                p, l = attention.softmax_rows(s)
+                o[qs, h], lse[h, qs] = p @ vh, l
+                dp = do[qs, h] @ vh.T
+                ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+                dq[qs, h] = scale * (ds @ kh)
+                dk[ks, h // G] += scale * (ds.T @ qh)
+                dv[ks, h // G] += p.T @ do[qs, h]
+        return (o, lse), (dq, dk, dv)
+
+    def fwd(q, k, v, cu_q, cu_k, causal, scale, window=-1):
+        return run(q, k, v, np.zeros_like(q), cu_q, cu_k, causal, scale, window)[0]
+
+    def bwd(q, k, v, do, cu_q, cu_k, causal, scale, window=-1):
+        return run(q, k, v, do, cu_q, cu_k, causal, scale, window)[1]
+    return fwd, bwd
+
+
+@pytest.mark.parametrize("mutant", ["key_overrun", "global_diagonal"])
+def test_varlen_mutants_fail_a_pin(mutant):
+    fwd, bwd = _varlen_factory(key_overrun=mutant == "key_overrun", global_diagonal=mutant == "global_diagonal")
+    with pytest.raises((AssertionError, ValueError)):
+        pins.pin_varlen_padded(fwd, bwd)
+
+
+def test_unmutated_varlen_factory_passes():
+    pins.pin_varlen_padded(*_varlen_factory())
