@@ -20,8 +20,15 @@
  *
  * Layout: Q, K, V, O, dO, dQ, dK, dV are contiguous row-major [B, H, N, D];
  * lse is contiguous float32 [B, H, N]. Query and key lengths are equal except
- * in fa_fwd_general / fa_bwd_general, and K/V heads may be fewer than query
- * heads in the _gqa and _general entry points.
+ * in the _general, _strided and _varlen entry points, and K/V heads may be
+ * fewer than query heads in all of those and the _gqa ones. The _strided entry
+ * points take any element strides for the batch, head and row dimensions (the
+ * head dimension D contiguous); the _varlen ones take packed variable-length
+ * batches.
+ *
+ * Rows that keep no key (causal with Nk < Nq leaves the first Nq - Nk rows
+ * so; a packed sequence may have no keys): O = 0, lse = -inf, and their
+ * gradients are 0 -- the sum over their keys is empty.
  *
  * Ownership: the caller allocates and owns every buffer (device memory).
  * The library never allocates, frees or synchronises, and keeps no state
@@ -104,19 +111,65 @@ int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
  *            every key, as when new queries extend a cached prefix of keys
  *            (the KV-cache prefill of the FlashPrefill V2 entry on the
  *            "FlashAttention" entity trail page, section "Corpus findings").
- *            Needs Nk >= Nq (otherwise the first rows would keep no key).
+ *            With Nk < Nq the first Nq - Nk rows keep no key (O = 0,
+ *            lse = -inf).
  *   window : -1, or w >= 0 to keep only keys j >= i + (Nk - Nq) - w -- with
  *            causal, a sliding window of the w + 1 keys ending at the
  *            diagonal (the local sliding-window attention of the WAND entry
  *            on the "attention mechanism" tag page). Tiles wholly outside a
  *            row's keys are skipped.
  * Nq = Nk = N with window = -1 is fa_fwd_gqa. Other arguments as for
- * fa_fwd; FA_ERR_INVALID_ARG also for Nk < 1, a K/V head of 2^31 bytes or
- * more, causal with Nk < Nq, or window < -1.
+ * fa_fwd; FA_ERR_INVALID_ARG also for Nk < 1 or window < -1.
  */
 int fa_fwd_general(const void* q, const void* k, const void* v, void* o,
                    float* lse, int B, int H, int Hkv, int Nq, int Nk, int D,
                    int causal, int window, float scale, int dtype, void* stream);
+
+/*
+ * Strided forward: fa_fwd_general on tensors with any element strides, e.g.
+ * [B, N, H, D] (the layout of a projection output viewed per head) or views of
+ * a packed QKV tensor. The pages name general strides only as part of the
+ * KV-cache prefill and batching work (FlashPrefill V2 entry, "FlashAttention"
+ * entity trail page, section "Corpus findings"); the layout is the caller's.
+ *   strides : host array of 14 element strides -- q (batch, head, row),
+ *             k (batch, head, row), v (batch, head, row), o (batch, head, row),
+ *             lse (batch, head). Element (b, h, i, d) of q is
+ *             q[b*s0 + h*s1 + i*s2 + d]; lse rows are contiguous. Read during
+ *             the call only.
+ * FA_ERR_INVALID_ARG if strides is NULL, a stride is negative, a row stride
+ * is < D, or a batch/head/row stride of q, k, v, o is not a multiple of 16
+ * bytes; FA_ERR_UNSUPPORTED if one head's rows (plus a tile of padding rows)
+ * span 2^31 bytes or more. Other arguments as for fa_fwd_general.
+ */
+int fa_fwd_strided(const void* q, const void* k, const void* v, void* o,
+                   float* lse, int B, int H, int Hkv, int Nq, int Nk, int D,
+                   int causal, int window, float scale, int dtype,
+                   const long long* strides, void* stream);
+
+/*
+ * Variable-length forward over a packed batch: B independent sequences whose
+ * rows are concatenated (the continuous batching of the FlashPrefill V2 entry
+ * on the "FlashAttention" entity trail page, section "Corpus findings").
+ *   q, o          : [total_q, H, D];  k, v : [total_k, Hkv, D];
+ *   lse           : [H, total_q] float.
+ *   cu_seqlens_q  : device int32 [B + 1]: sequence b is rows
+ *                   cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of q, o and lse;
+ *                   cu_seqlens_k likewise for k and v. Offsets must be
+ *                   non-decreasing from 0 to total; the kernels clamp them into
+ *                   [0, total] (so no access leaves the tensors) but rows of
+ *                   malformed sequences are then not defined.
+ *   max_seqlen_q, max_seqlen_k : upper bounds of the lengths (they size the
+ *                   launch; rows past them are not computed).
+ * causal and window apply inside each sequence with its own lengths (the
+ * bottom-right diagonal of fa_fwd_general). Other arguments as for
+ * fa_fwd_general; FA_ERR_INVALID_ARG also for a NULL or misaligned offset
+ * array or total_q, total_k < 1.
+ */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
+                  float* lse, const int* cu_seqlens_q, const int* cu_seqlens_k,
+                  int B, int H, int Hkv, int total_q, int total_k,
+                  int max_seqlen_q, int max_seqlen_k, int D, int causal,
+                  int window, float scale, int dtype, void* stream);
 
 /*
  * fa_fwd with an explicit conditional-rescale threshold `rescale_log2`
@@ -225,6 +278,38 @@ int fa_bwd_general(const void* q, const void* k, const void* v, const void* o,
                    void* dv, int B, int H, int Hkv, int Nq, int Nk, int D,
                    int causal, int window, float scale, int dtype, int variant,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Strided backward: the gradients of fa_fwd_strided.
+ *   strides : host array of 26 element strides -- (batch, head, row) of q, k,
+ *             v, o, dO, dq, dk, dv in that order, then lse (batch, head).
+ *   workspace : fa_bwd_workspace_size(B, H, Nq, D, dtype, variant) bytes.
+ * Errors as for fa_fwd_strided and fa_bwd_general; the span limit applies to
+ * the rows of the H / Hkv query heads that share a K/V head, which one pass
+ * reads together.
+ */
+int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o,
+                   const void* dO, const float* lse, void* dq, void* dk,
+                   void* dv, int B, int H, int Hkv, int Nq, int Nk, int D,
+                   int causal, int window, float scale, int dtype, int variant,
+                   void* workspace, size_t workspace_bytes,
+                   const long long* strides, void* stream);
+
+/*
+ * Variable-length backward: the gradients of fa_fwd_varlen.
+ *   q, o, dO, dq : [total_q, H, D];  k, v, dk, dv : [total_k, Hkv, D];
+ *   lse          : [H, total_q];  workspace: fa_bwd_workspace_size(1, H,
+ *                  total_q, D, dtype, variant) bytes.
+ * Key rows outside every sequence are not written. Other arguments and errors
+ * as for fa_fwd_varlen and fa_bwd_general.
+ */
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                  const void* dO, const float* lse, void* dq, void* dk,
+                  void* dv, const int* cu_seqlens_q, const int* cu_seqlens_k,
+                  int B, int H, int Hkv, int total_q, int total_k,
+                  int max_seqlen_q, int max_seqlen_k, int D, int causal,
+                  int window, float scale, int dtype, int variant,
+                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * dK and dV only: the preprocess and the key-tile pass of fa_bwd, without any

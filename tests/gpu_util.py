@@ -30,13 +30,14 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu", torch.float64).numpy()
 
 
-def prepare(dtype: str, shape, seed: int, multiplier: float = 1.0, with_grad: bool = False, hkv=None, nk=None):
+def prepare(dtype: str, shape, seed: int, multiplier: float = 1.0, with_grad: bool = False, hkv=None, nk=None,
+            kv_shape=None):
     """Draw Q, K, V (and dO) and return (device tensors dict, float64 oracle inputs dict).
 
-    hkv, nk: K/V head count and key length when they differ from Q's (K and V get [B, hkv, nk, D]).
+    hkv, nk: K/V head count and key length when they differ from Q's (K and V get [B, hkv, nk, D]);
+    kv_shape: K/V's whole shape instead (e.g. for packed [total, heads, D] tensors).
     """
-    kv_shape = None
-    if hkv is not None or nk is not None:
+    if kv_shape is None and (hkv is not None or nk is not None):
         kv_shape = (shape[0], shape[1] if hkv is None else hkv, shape[2] if nk is None else nk, shape[3])
     arrs = inputs.draw(tuple(shape), seed, 4 if with_grad else 3, multiplier, kv_shape=kv_shape)
     names = ["q", "k", "v", "do"][: len(arrs)]

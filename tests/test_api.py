@@ -181,7 +181,7 @@ def test_bwd_gqa_validation():
     assert call(8, 2, wsb=ws - 1) == fa.FA_ERR_WORKSPACE
     # 64 query heads of 2^20 x 64 bf16 (2^27 bytes each) share one K/V head: the group spans 2^33 bytes
     big = fa.bwd_workspace_size(1, 64, 1 << 20, 64, fa.FA_BWD_DETERMINISTIC)
-    assert call(64, 1, N=1 << 20, wsb=big) == fa.FA_ERR_UNSUPPORTED and "2^32" in fa.last_error()
+    assert call(64, 1, N=1 << 20, wsb=big) == fa.FA_ERR_UNSUPPORTED and "2^31" in fa.last_error()
 
 
 def _fwd_general(**kw):
@@ -195,10 +195,9 @@ def _fwd_general(**kw):
 @pytest.mark.parametrize("kw,status,msg", [
     (dict(Nk=0), fa.FA_ERR_INVALID_ARG, "Nk"),
     (dict(Nq=0), fa.FA_ERR_INVALID_ARG, ">= 1"),
-    (dict(Nq=40, Nk=32, causal=1), fa.FA_ERR_INVALID_ARG, "Nk >= Nq"),
     (dict(window=-2), fa.FA_ERR_INVALID_ARG, "window"),
     (dict(Hkv=3), fa.FA_ERR_INVALID_ARG, "divide"),
-    (dict(Nk=1 << 24, D=128, Nq=16), fa.FA_ERR_INVALID_ARG, "2^31"),
+    (dict(Nk=1 << 24, D=128, Nq=16), fa.FA_ERR_UNSUPPORTED, "2^31"),
     (dict(D=96), fa.FA_ERR_UNSUPPORTED, "D=96"),
     (dict(k=None), fa.FA_ERR_INVALID_ARG, "NULL"),
 ])
@@ -215,7 +214,6 @@ def test_bwd_general_validation():
         return L.fa_bwd_general(P, P, P, P, P, P, P, P, P, 1, 2, 1, Nq, Nk, 64, causal, window, 0.1, dtype, variant,
                                 P, wsb, None)
 
-    assert call(Nq=40, Nk=32) == fa.FA_ERR_INVALID_ARG and "Nk >= Nq" in fa.last_error()
     assert call(window=-5) == fa.FA_ERR_INVALID_ARG and "window" in fa.last_error()
     assert call(Nk=0) == fa.FA_ERR_INVALID_ARG
     assert call(variant=2) == fa.FA_ERR_INVALID_ARG
@@ -232,3 +230,90 @@ def test_binding_argument_counts_match_header():
         params = params.strip()
         n = 0 if params in ("", "void") else len(params.split(","))
         assert len(getattr(L, name).argtypes) == n, (name, n, len(getattr(L, name).argtypes))
+
+
+def _fwd_strided(strides=None, **kw):
+    a = dict(B=2, H=4, Hkv=2, Nq=16, Nk=32, D=64, causal=1, window=-1, scale=0.125, dtype=fa.FA_BF16)
+    a.update(kw)
+    B, H, Hkv, Nq, Nk, D = a["B"], a["H"], a["Hkv"], a["Nq"], a["Nk"], a["D"]
+    if strides is None:  # [B, N, H, D] views
+        strides = [Nq * H * D, D, H * D, Nk * Hkv * D, D, Hkv * D, Nk * Hkv * D, D, Hkv * D, Nq * H * D, D, H * D,
+                   H * Nq, Nq]
+    arr = None if strides == "null" else (ctypes.c_longlong * 14)(*strides)
+    return fa.lib().fa_fwd_strided(P, P, P, P, P, B, H, Hkv, Nq, Nk, D, a["causal"], a["window"], a["scale"],
+                                   a["dtype"], arr, None)
+
+
+def _bnhd(B, H, Hkv, Nq, Nk, D):
+    q = [Nq * H * D, D, H * D]
+    k = [Nk * Hkv * D, D, Hkv * D]
+    return q, k
+
+
+@pytest.mark.parametrize("edit,status,msg", [
+    ("null", fa.FA_ERR_INVALID_ARG, "strides is NULL"),
+    ({0: -1}, fa.FA_ERR_INVALID_ARG, "q strides"),
+    ({5: 63}, fa.FA_ERR_INVALID_ARG, "row stride >= D"),
+    ({2: 260}, fa.FA_ERR_INVALID_ARG, "16 bytes"),      # q rows 520 bytes apart
+    ({4: 68}, fa.FA_ERR_INVALID_ARG, "16 bytes"),       # k heads 136 bytes apart
+    ({11: 1 << 23}, fa.FA_ERR_UNSUPPORTED, "2^31"),     # o rows 2^24 bytes apart
+    ({12: -4}, fa.FA_ERR_INVALID_ARG, "lse strides"),
+])
+def test_fwd_strided_validation(edit, status, msg):
+    if edit == "null":
+        st = "null"
+    else:
+        st = [2 * 16 * 4 * 64, 64, 4 * 64, 32 * 2 * 64, 64, 2 * 64, 32 * 2 * 64, 64, 2 * 64, 16 * 4 * 64, 64, 4 * 64,
+              64, 16]
+        for i, v in edit.items():
+            st[i] = v
+    assert _fwd_strided(st) == status
+    assert msg in fa.last_error()
+
+
+def test_bwd_strided_validation():
+    L = fa.lib()
+    B, H, Hkv, Nq, Nk, D = 1, 4, 2, 16, 32, 64
+    ws = fa.bwd_workspace_size(B, H, Nq, D, fa.FA_BWD_DETERMINISTIC)
+    q, k = _bnhd(B, H, Hkv, Nq, Nk, D)
+    good = q + k + k + q + q + q + k + k + [H * Nq, Nq]
+
+    def call(st, variant=fa.FA_BWD_DETERMINISTIC, wsb=ws):
+        arr = None if st is None else (ctypes.c_longlong * 26)(*st)
+        return L.fa_bwd_strided(P, P, P, P, P, P, P, P, P, B, H, Hkv, Nq, Nk, D, 1, -1, 0.1, fa.FA_BF16, variant, P,
+                                wsb, arr, None)
+
+    assert call(None) == fa.FA_ERR_INVALID_ARG and "NULL" in fa.last_error()
+    assert call(good, variant=5) == fa.FA_ERR_INVALID_ARG and "variant" in fa.last_error()
+    assert call(good, wsb=ws - 1) == fa.FA_ERR_WORKSPACE
+    for i, name in ((14, "dO"), (17, "dq"), (20, "dk"), (23, "dv")):
+        bad = list(good)
+        bad[i] = D - 8  # row stride below D
+        assert call(bad) == fa.FA_ERR_INVALID_ARG and name in fa.last_error(), name
+    bad = list(good)
+    bad[13] = 1 << 30  # dO heads 2^31 bytes apart: the 2 query heads of a group cannot share one 32-bit range
+    assert call(bad) == fa.FA_ERR_UNSUPPORTED and "dO" in fa.last_error()
+
+
+def test_varlen_validation():
+    L = fa.lib()
+    B, H, Hkv, D, Tq, Tk = 3, 4, 2, 64, 100, 150
+    ws = fa.bwd_workspace_size(1, H, Tq, D, fa.FA_BWD_DETERMINISTIC)
+
+    def f(cu_q=P, cu_k=P, Tq=Tq, Tk=Tk, mq=50, mk=60, D=D):
+        return L.fa_fwd_varlen(P, P, P, P, P, cu_q, cu_k, B, H, Hkv, Tq, Tk, mq, mk, D, 1, -1, 0.125, fa.FA_BF16,
+                               None)
+
+    def b(wsb=ws, variant=fa.FA_BWD_DETERMINISTIC, cu_k=P):
+        return L.fa_bwd_varlen(P, P, P, P, P, P, P, P, P, P, cu_k, B, H, Hkv, Tq, Tk, 50, 60, D, 1, -1, 0.125,
+                               fa.FA_BF16, variant, P, wsb, None)
+
+    assert f(cu_q=None) == fa.FA_ERR_INVALID_ARG and "cu_seqlens_q" in fa.last_error()
+    assert f(cu_k=None) == fa.FA_ERR_INVALID_ARG and "cu_seqlens_k" in fa.last_error()
+    assert f(cu_q=P + 2) == fa.FA_ERR_INVALID_ARG and "aligned" in fa.last_error()
+    assert f(Tq=0) == fa.FA_ERR_INVALID_ARG and "total" in fa.last_error()
+    assert f(mq=0) == fa.FA_ERR_INVALID_ARG
+    assert f(D=80) == fa.FA_ERR_UNSUPPORTED
+    assert b(wsb=ws - 1) == fa.FA_ERR_WORKSPACE
+    assert b(variant=2) == fa.FA_ERR_INVALID_ARG
+    assert b(cu_k=None) == fa.FA_ERR_INVALID_ARG

@@ -34,49 +34,63 @@ constexpr float kInf = __builtin_huge_valf();
 // ld[rows + row] = -D with D = sum_d dO O (negated so it can initialise the
 // dP accumulator, which then holds dP - D for free); the atomic variant also
 // zeroes dQ_accum. One thread per 8 consecutive elements of a row.
+//
+// Workspace row r = (b * H + h) * Np + i is query row i of head h of entry b
+// (packed sequences: Bp = 1 and i runs over all packed rows, which is the
+// same row as cu_q[b] + i of entry b). A row that kept no key (lse = -inf)
+// gets +inf, so every recomputed probability of it is 2^-inf = 0.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ void __launch_bounds__(256) bwd_pre_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ dO,
-                                                      const float* __restrict__ lse, float* __restrict__ ld,
-                                                      float* __restrict__ dq_accum, long long rows) {
+__global__ void __launch_bounds__(256) bwd_pre_kernel(BwdParams P, int H, int Np) {
   constexpr int TPR = D / 8;  // threads per row
   const long long gt = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long row = gt / TPR;
   const int part = (int)(gt % TPR);
+  const bool in = row < P.rows;
+  const int r = in ? (int)row : 0;  // rows < 2^29
+  const int i = r % Np, bh = r / Np, h = bh % H, b = bh / H;
   float s = 0.f;
-  if (row < rows) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(o + row * D + part * 8);
-    const bf16x8 b = *reinterpret_cast<const bf16x8*>(dO + row * D + part * 8);
+  if (in) {
+    const __bf16* o = static_cast<const __bf16*>(P.o) + (b * P.so.b + h * P.so.h + i * P.so.r) + part * 8;
+    const __bf16* dO = static_cast<const __bf16*>(P.dO) + (b * P.sdo.b + h * P.sdo.h + i * P.sdo.r) + part * 8;
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(o);
+    const bf16x8 y = *reinterpret_cast<const bf16x8*>(dO);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) s += (float)a[i] * (float)b[i];
-    if (dq_accum) {
-      f32x4* z = reinterpret_cast<f32x4*>(dq_accum + row * D + part * 8);
+    for (int j = 0; j < 8; ++j) s += (float)x[j] * (float)y[j];
+    if (P.dq_accum) {
+      f32x4* z = reinterpret_cast<f32x4*>(P.dq_accum + row * D + part * 8);
       z[0] = f32x4{};
       z[1] = f32x4{};
     }
   }
 #pragma unroll
   for (int o2 = TPR / 2; o2 > 0; o2 >>= 1) s += __shfl_xor(s, o2, 64);
-  if (row < rows && part == 0) {
-    ld[row] = lse[row] * kLog2e;
-    ld[rows + row] = -s;
+  if (in && part == 0) {
+    const float l = P.lse[b * P.lse_b + h * P.lse_h + i];
+    P.ld[row] = l == -kInf ? kInf : l * kLog2e;
+    P.ld[P.rows + row] = -s;
   }
 }
 
-// dQ = bf16(dQ_accum) (the scale is already applied).
-__global__ void __launch_bounds__(256) bwd_dq_convert_kernel(const float* __restrict__ acc, __bf16* __restrict__ dq,
-                                                             long long n8) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  const f32x4 a = *reinterpret_cast<const f32x4*>(acc + 8 * i);
-  const f32x4 b = *reinterpret_cast<const f32x4*>(acc + 8 * i + 4);
-  bf16x8 r;
+// dQ = bf16(dQ_accum) (the scale is already applied); rows as in bwd_pre_kernel.
+template <int D>
+__global__ void __launch_bounds__(256) bwd_dq_convert_kernel(BwdParams P, int H, int Np) {
+  constexpr int TPR = D / 8;
+  const long long gt = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long row = gt / TPR;
+  if (row >= P.rows) return;
+  const int part = (int)(gt % TPR);
+  const int r = (int)row;
+  const int i = r % Np, bh = r / Np, h = bh % H, b = bh / H;
+  const f32x4 a = *reinterpret_cast<const f32x4*>(P.dq_accum + row * D + part * 8);
+  const f32x4 c = *reinterpret_cast<const f32x4*>(P.dq_accum + row * D + part * 8 + 4);
+  bf16x8 v;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    r[j] = (__bf16)a[j];
-    r[4 + j] = (__bf16)b[j];
+    v[j] = (__bf16)a[j];
+    v[4 + j] = (__bf16)c[j];
   }
-  *reinterpret_cast<bf16x8*>(dq + 8 * i) = r;
+  *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(P.dq) + (b * P.sdq.b + h * P.sdq.h + i * P.sdq.r) + part * 8) = v;
 }
 
 // ---------------------------------------------------------------------------
@@ -115,62 +129,65 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
 
   // Workgroup -> (K/V head, key tile); under causal masking the first key
   // tiles see the most query tiles: rank 0 is key tile 0. The K/V head's
-  // `group` query heads are consecutive ([qbh0, qbh0 + group)), so their Q, dO
-  // and per-row values form one contiguous range of group*N rows: the pass
-  // walks the query tiles of every head of the group, which sums their dK and
-  // dV contributions in the accumulators.
+  // `group` query heads are consecutive (h0 .. h0 + group - 1): the pass walks
+  // the query tiles of every head of the group, which sums their dK and dV
+  // contributions in the accumulators.
   int bh, kt;
   wg_map(n_ktiles, P.causal, 1, bh, kt);
-  const int N = P.N;  // query rows per head
-  const KeyBounds kb{N, P.Nk, P.causal, P.window};
   const int group = P.group;
   const int hkv = P.hq / group;
-  const int qbh0 = (bh / hkv) * P.hq + (bh % hkv) * group;
+  const int b = bh / hkv, hk = bh % hkv, h0 = hk * group;
+  const Seq sq = seq_of(P.cu_q, P.cu_k, b, P.N, P.Nk, P.total_q, P.total_k);
+  const int N = sq.nq;   // query rows per head of this entry
+  const int NK = sq.nk;  // keys of this entry
   const int k0 = kt * C::BK;
+  if (k0 >= NK) return;  // whole workgroup: a short packed sequence has fewer key tiles
+  const KeyBounds kb{N, NK, P.causal, P.window};
   const int kw = k0 + 32 * wave;
   const int key = kw + li;
 
-  const size_t head = (size_t)bh * P.Nk * D;     // K/V head
-  const size_t qhead = (size_t)qbh0 * N * D;     // first query head of the group
-  const uint32_t head_bytes = (uint32_t)((size_t)P.Nk * D * 2);
-  const uint32_t group_bytes = (uint32_t)((size_t)group * N * D * 2);
-  const auto rq = make_rsrc(reinterpret_cast<const __bf16*>(P.q) + qhead, group_bytes);
-  const auto rk = make_rsrc(reinterpret_cast<const __bf16*>(P.k) + head, head_bytes);
-  const auto rv = make_rsrc(reinterpret_cast<const __bf16*>(P.v) + head, head_bytes);
-  const auto rdo = make_rsrc(reinterpret_cast<const __bf16*>(P.dO) + qhead, group_bytes);
-  // lse*log2e rows of the group's query heads, and their -D rows `rows` floats further on
-  const size_t rows = (size_t)P.rows;
-  const auto rld = make_rsrc(P.ld, (uint32_t)(rows * 8));
-  const uint32_t ld_l2 = (uint32_t)((size_t)qbh0 * N * 4), ld_nd = (uint32_t)((rows + (size_t)qbh0 * N) * 4);
+  const long long bb = P.cu_q ? 0 : b;  // packed sequences start at rows tq / tk instead
+  const __bf16* qg = static_cast<const __bf16*>(P.q) + (bb * P.sq.b + h0 * P.sq.h + sq.tq * P.sq.r);
+  const __bf16* dog = static_cast<const __bf16*>(P.dO) + (bb * P.sdo.b + h0 * P.sdo.h + sq.tq * P.sdo.r);
+  const __bf16* kh = static_cast<const __bf16*>(P.k) + (bb * P.sk.b + hk * P.sk.h + sq.tk * P.sk.r);
+  const __bf16* vh = static_cast<const __bf16*>(P.v) + (bb * P.sv.b + hk * P.sv.h + sq.tk * P.sv.r);
+  const uint32_t qrs = (uint32_t)(P.sq.r * 2), dors = (uint32_t)(P.sdo.r * 2);
+  const uint32_t qhs = (uint32_t)(P.sq.h * 2), dohs = (uint32_t)(P.sdo.h * 2);
+  const uint32_t krs = (uint32_t)(P.sk.r * 2), vrs = (uint32_t)(P.sv.r * 2);
+  // Q and dO of the whole group: head g's row i is at g * (head stride) + i * (row stride)
+  const auto rq = make_rsrc(qg, N > 0 ? (uint32_t)(group - 1) * qhs + head_span(N, qrs, RB) : 0u);
+  const auto rdo = make_rsrc(dog, N > 0 ? (uint32_t)(group - 1) * dohs + head_span(N, dors, RB) : 0u);
+  const auto rk = make_rsrc(kh, head_span(NK, krs, RB));
+  const auto rv = make_rsrc(vh, head_span(NK, vrs, RB));
+  // lse*log2e of workspace row r at 4r, its -D at 4(rows + r); the group's
+  // head g, query i is workspace row ld_row0 + g * ld_h + i.
+  const auto rld = make_rsrc(P.ld, (uint32_t)(P.rows * 8));
+  const uint32_t ld_row0 = (uint32_t)(bb * P.ld_b + h0 * P.ld_h + sq.tq), ld_h = (uint32_t)P.ld_h;
+  const uint32_t ld_nd = (uint32_t)(P.rows * 4);
 
   // K^T and V^T pieces (B operands of S = Q K^T and dP = dO V^T).
   i32x4 kf[NP], vf[NP];
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
-    kf[p] = buf_load16(rk, (uint32_t)key * RB + 32 * p + 16 * hf);
-    vf[p] = buf_load16(rv, (uint32_t)key * RB + 32 * p + 16 * hf);
+    kf[p] = buf_load16(rk, (uint32_t)key * krs + 32 * p + 16 * hf);
+    vf[p] = buf_load16(rv, (uint32_t)key * vrs + 32 * p + 16 * hf);
   }
 
-  uint32_t goff[C::LPW];
-#pragma unroll
-  for (int i = 0; i < C::LPW; ++i) {
-    int row, ch;
-    tile_pos<RB>((wave * C::LPW + i) * 64 + lane, row, ch);
-    goff[i] = (uint32_t)(row * RB + ch * 16);
-  }
-  // row0: first row of the tile within the group's rows (g * N + q0 for head g)
-  auto issue = [&](int row0, char* st) {
-    const uint32_t base = (uint32_t)row0 * RB;
+  static_assert(tile_rows_affine_ok<RB, C::LPW, C::NW>(), "loader rows");
+  const TileLoader<C::LPW, RB> tl(wave, lane, qrs, dors);
+  // Query tile of head g of the group starting at query i0.
+  auto issue = [&](int g, int i0, char* st) {
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i) {
       const int m = wave * C::LPW + i;
-      buf_load_lds16(rq, goff[i] + base, 0, (lds_void*)(st + m * 1024));
-      buf_load_lds16(rdo, goff[i] + base, 0, (lds_void*)(st + C::OFF_DO + m * 1024));
+      buf_load_lds16(rq, tl.a(i, i0) + (uint32_t)g * qhs, 0, (lds_void*)(st + m * 1024));
+      buf_load_lds16(rdo, tl.b(i, i0) + (uint32_t)g * dohs, 0, (lds_void*)(st + C::OFF_DO + m * 1024));
     }
-    // lanes 0..BQ/4-1 bring lse*log2e of the tile's rows, the next BQ/4 lanes their -D
-    if (wave == 0 && lane < BQ / 2) {
-      const int half = lane >= BQ / 4, j = lane - half * (BQ / 4);
-      buf_load_lds16(rld, (half ? ld_nd : ld_l2) + (uint32_t)(row0 * 4 + j * 16), 0, (lds_void*)(st + C::OFF_LD));
+    // lanes 0..BQ-1 (of the first 2*BQ/64 waves) bring lse*log2e of the tile's rows, lanes BQ..2BQ-1 their -D
+    if (wave < 2 * BQ / 64) {
+      const int L = wave * 64 + lane, half = L >= BQ, j = L - half * BQ;
+      const uint32_t r = ld_row0 + (uint32_t)g * ld_h + (uint32_t)(i0 + j);
+      buf_load_lds4(rld, (half ? ld_nd : 0u) + 4 * r, (lds_void*)(st + C::OFF_LD + wave * 256));
     }
   };
 
@@ -182,7 +199,7 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
       const int m = wave * C::KLPW + i;
       int row, ch;
       tile_pos<RB>(m * 64 + lane, row, ch);
-      buf_load_lds16(rk, (uint32_t)((k0 + row) * RB + ch * 16), 0, (lds_void*)(kt_lds + m * 1024));
+      buf_load_lds16(rk, (uint32_t)(k0 + row) * krs + ch * 16, 0, (lds_void*)(kt_lds + m * 1024));
     }
   }
 
@@ -202,7 +219,7 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
 
   // query tiles [qt0, nq) hold every query that keeps a key of this workgroup
   const int qt0 = kb.qlo(k0) / BQ;
-  const int nq = kb.qhi(min(k0 + C::BK, P.Nk) - 1) / BQ + 1;
+  const int nq = kb.qhi(min(k0 + C::BK, NK) - 1) / BQ + 1;
   const float sl2 = P.scale_log2;
 
   // Query tiles visited, head by head of the group: (hg, it) runs over
@@ -216,7 +233,7 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
   };
   // (a window can leave the first keys with no query at all: then dK = dV = 0)
   if (qt0 < nq) {
-    issue(qt0 * BQ, smem);
+    issue(0, qt0 * BQ, smem);
     wait_vmem();
   }
   __syncthreads();
@@ -232,7 +249,7 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
     int nhg = hg, nit = it;
     advance(nhg, nit);
     const bool more = nhg < group;
-    if (more) issue(nhg * N + nit * BQ, nxt);
+    if (more) issue(nhg, nit * BQ, nxt);
     const char* qs = cur;
     const char* dos = qs + C::OFF_DO;
     const float* lds_ld = reinterpret_cast<const float*>(qs + C::OFF_LD);
@@ -374,7 +391,7 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
                               lds_read_tr16(ktb + tr16_off<RB, false>(lane, e, 1) + kc * 16 * RB)};
           c = mfma_bf16(__builtin_bit_cast(bf16x8, x), __builtin_bit_cast(bf16x8, y), c);
         }
-        float* dst = P.dq_accum + ((size_t)(qbh0 + qh) * N) * D + 32 * e + li;
+        float* dst = P.dq_accum + ((size_t)ld_row0 + (size_t)qh * ld_h) * D + 32 * e + li;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int q = q0 + 32 * a + (v >> 2) * 8 + 4 * hf + (v & 3);
@@ -393,9 +410,9 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
     if (hg < group) tile(smem + C::STAGE, smem, ds_lds, kt_lds);
   }
 
-  if (key < P.Nk) {
-    __bf16* dk = reinterpret_cast<__bf16*>(P.dk) + head + (size_t)key * D;
-    __bf16* dv = reinterpret_cast<__bf16*>(P.dv) + head + (size_t)key * D;
+  if (key < NK) {
+    __bf16* dk = static_cast<__bf16*>(P.dk) + (bb * P.sdk.b + hk * P.sdk.h + (sq.tk + key) * P.sdk.r);
+    __bf16* dv = static_cast<__bf16*>(P.dv) + (bb * P.sdv.b + hk * P.sdv.h + (sq.tk + key) * P.sdv.r);
 #pragma unroll
     for (int e = 0; e < NE; ++e)
 #pragma unroll
@@ -441,48 +458,51 @@ bwd_dq_kernel(BwdParams P, int n_qtiles) {
 
   int bh, qt;
   wg_map(n_qtiles, P.causal, P.group, bh, qt);
-  if (P.causal) qt = n_qtiles - 1 - qt;
-  const int N = P.N;
+  const int b = bh / P.hq, h = bh % P.hq, hk = h / P.group;
+  const Seq sq = seq_of(P.cu_q, P.cu_k, b, P.N, P.Nk, P.total_q, P.total_k);
+  const int N = sq.nq;
+  const int n_qt = (N + C::BM - 1) / C::BM;
+  if (P.causal) qt = n_qt - 1 - qt;
+  if (qt < 0 || qt >= n_qt) return;  // whole workgroup
   const int q0 = qt * C::BM;
   const int qw = q0 + 32 * wave;
   const int qrow = qw + li;
 
-  const KeyBounds kb{N, P.Nk, P.causal, P.window};
-  const size_t head = (size_t)bh * N * D;
-  const size_t kvhead = (size_t)kv_head(bh, P.hq, P.group) * P.Nk * D;
-  const uint32_t head_bytes = (uint32_t)((size_t)N * D * 2), kv_bytes = (uint32_t)((size_t)P.Nk * D * 2);
-  const auto rq = make_rsrc(reinterpret_cast<const __bf16*>(P.q) + head, head_bytes);
-  const auto rk = make_rsrc(reinterpret_cast<const __bf16*>(P.k) + kvhead, kv_bytes);
-  const auto rv = make_rsrc(reinterpret_cast<const __bf16*>(P.v) + kvhead, kv_bytes);
-  const auto rdo = make_rsrc(reinterpret_cast<const __bf16*>(P.dO) + head, head_bytes);
+  const KeyBounds kb{N, sq.nk, P.causal, P.window};
+  const long long bb = P.cu_q ? 0 : b;
+  const __bf16* qh = static_cast<const __bf16*>(P.q) + (bb * P.sq.b + h * P.sq.h + sq.tq * P.sq.r);
+  const __bf16* doh = static_cast<const __bf16*>(P.dO) + (bb * P.sdo.b + h * P.sdo.h + sq.tq * P.sdo.r);
+  const __bf16* kh = static_cast<const __bf16*>(P.k) + (bb * P.sk.b + hk * P.sk.h + sq.tk * P.sk.r);
+  const __bf16* vh = static_cast<const __bf16*>(P.v) + (bb * P.sv.b + hk * P.sv.h + sq.tk * P.sv.r);
+  const uint32_t qrs = (uint32_t)(P.sq.r * 2), dors = (uint32_t)(P.sdo.r * 2);
+  const uint32_t krs = (uint32_t)(P.sk.r * 2), vrs = (uint32_t)(P.sv.r * 2);
+  const auto rq = make_rsrc(qh, head_span(N, qrs, RB));
+  const auto rdo = make_rsrc(doh, head_span(N, dors, RB));
+  const auto rk = make_rsrc(kh, head_span(sq.nk, krs, RB));
+  const auto rv = make_rsrc(vh, head_span(sq.nk, vrs, RB));
 
   i32x4 qf[NP], dof[NP];
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
-    qf[p] = buf_load16(rq, (uint32_t)qrow * RB + 32 * p + 16 * hf);
-    dof[p] = buf_load16(rdo, (uint32_t)qrow * RB + 32 * p + 16 * hf);
+    qf[p] = buf_load16(rq, (uint32_t)qrow * qrs + 32 * p + 16 * hf);
+    dof[p] = buf_load16(rdo, (uint32_t)qrow * dors + 32 * p + 16 * hf);
   }
   float lse_l2 = kInf, dlt = 0.f;
   if (qrow < N) {
-    lse_l2 = P.ld[(size_t)bh * N + qrow];
-    dlt = -P.ld[(size_t)P.rows + (size_t)bh * N + qrow];
+    const size_t r = (size_t)(bb * P.ld_b + h * P.ld_h + sq.tq) + qrow;  // workspace row
+    lse_l2 = P.ld[r];
+    dlt = -P.ld[(size_t)P.rows + r];
   }
   const float sl2 = P.scale_log2;
 
-  uint32_t goff[C::LPW];
-#pragma unroll
-  for (int i = 0; i < C::LPW; ++i) {
-    int row, ch;
-    tile_pos<RB>((wave * C::LPW + i) * 64 + lane, row, ch);
-    goff[i] = (uint32_t)(row * RB + ch * 16);
-  }
+  static_assert(tile_rows_affine_ok<RB, C::LPW, C::NW>(), "loader rows");
+  const TileLoader<C::LPW, RB> tl(wave, lane, krs, vrs);
   auto issue = [&](int key0, char* kb) {
-    const uint32_t base = (uint32_t)key0 * RB;
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i) {
       const int m = wave * C::LPW + i;
-      buf_load_lds16(rk, goff[i] + base, 0, (lds_void*)(kb + m * 1024));
-      buf_load_lds16(rv, goff[i] + base, 0, (lds_void*)(kb + C::TILE + m * 1024));
+      buf_load_lds16(rk, tl.a(i, key0), 0, (lds_void*)(kb + m * 1024));
+      buf_load_lds16(rv, tl.b(i, key0), 0, (lds_void*)(kb + C::TILE + m * 1024));
     }
   };
   // One base register per operand kind (see the key-tile pass).
@@ -552,7 +572,7 @@ bwd_dq_kernel(BwdParams P, int n_qtiles) {
       // wave-uniform branch (see the key-tile pass). Element (b, v) is key
       // key0 + 4h + r with r = 32b + 8(v/4) + v%4, kept iff
       // key_lo(qrow) <= key <= key_hi(qrow).
-      if ((key0 + BN > kb.nk) || (P.causal && key0 + BN - 1 > kb.hi(qw)) || (kb.window >= 0 && key0 < kb.lo(qw + 31))) {
+      if (kb.mask_tile<BN>(key0, qw)) {
         int hi = kb.hi(qrow) - key0 - 4 * hf, lo = kb.lo(qrow) - key0 - 4 * hf;
         opaque(hi);
         opaque(lo);
@@ -602,7 +622,7 @@ bwd_dq_kernel(BwdParams P, int n_qtiles) {
   }
 
   if (qrow < N) {
-    __bf16* dq = reinterpret_cast<__bf16*>(P.dq) + head + (size_t)qrow * D;
+    __bf16* dq = static_cast<__bf16*>(P.dq) + (bb * P.sdq.b + h * P.sdq.h + (sq.tq + qrow) * P.sdq.r);
 #pragma unroll
     for (int e = 0; e < NE; ++e)
 #pragma unroll
@@ -615,20 +635,20 @@ bwd_dq_kernel(BwdParams P, int n_qtiles) {
   }
 }
 
+// Workspace rows of the preprocess and the dQ convert: Bp entries of Np rows
+// per head (packed sequences: one entry of all packed rows).
 template <int D>
-static hipError_t launch_pre(const BwdParams& p, long long rows, hipStream_t st) {
-  const long long threads = rows * (D / 8);
-  hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
-                     reinterpret_cast<const __bf16*>(p.o), reinterpret_cast<const __bf16*>(p.dO), p.lse, p.ld,
-                     p.dq_accum, rows);
+static hipError_t launch_pre(const BwdParams& p, int H, hipStream_t st) {
+  const long long threads = p.rows * (D / 8);
+  const int Np = p.cu_q ? p.total_q : p.N;
+  hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, p, H, Np);
   return hipGetLastError();
 }
 
 template <class KCA, class KCD, class QC>
 static hipError_t launch_bwd(int variant, const BwdParams& p, int B, int H, hipStream_t st) {
-  const long long rows = (long long)B * H * p.N;
   const int HKV = H / p.group;  // the key-tile passes run over K/V heads
-  hipError_t e = launch_pre<KCD::D>(p, rows, st);
+  hipError_t e = launch_pre<KCD::D>(p, H, st);
   if (e != hipSuccess) return e;
   if (variant == 0) {
     const int nk = (p.Nk + KCA::BK - 1) / KCA::BK;
@@ -636,9 +656,9 @@ static hipError_t launch_bwd(int variant, const BwdParams& p, int B, int H, hipS
     if (gk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((bwd_dkdv_kernel<KCA, true>), dim3((unsigned)gk), dim3(KCA::NT), 0, st, p, nk);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const long long n8 = rows * KCA::D / 8;
-    hipLaunchKernelGGL(bwd_dq_convert_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, p.dq_accum,
-                       reinterpret_cast<__bf16*>(p.dq), n8);
+    const long long n8 = p.rows * KCA::D / 8;
+    const int Np = p.cu_q ? p.total_q : p.N;
+    hipLaunchKernelGGL(bwd_dq_convert_kernel<KCA::D>, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, p, H, Np);
     return hipGetLastError();
   }
   const int nk = (p.Nk + KCD::BK - 1) / KCD::BK;

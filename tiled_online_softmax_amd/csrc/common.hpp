@@ -75,7 +75,7 @@ __device__ __forceinline__ constexpr uint32_t tile_off(int row, int chunk) {
 
 // Inverse of tile_off: physical 16-byte slot -> (row, logical chunk).
 template <int RB>
-__device__ __forceinline__ void tile_pos(int phys, int& row, int& chunk) {
+__device__ __forceinline__ constexpr void tile_pos(int phys, int& row, int& chunk) {
   const int line = phys >> 4, pos = phys & 15;
   if constexpr (RB >= 256) {
     constexpr int LPR = RB / 256;
@@ -98,6 +98,33 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 __device__ __forceinline__ void buf_load_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
                                                lds_void* lds_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 16, (int)voff, (int)soff, 0, 0);
+}
+
+// 4 bytes per lane from a buffer straight into LDS at lds_base + 4 * lane.
+__device__ __forceinline__ void buf_load_lds4(__amdgpu_buffer_rsrc_t r, uint32_t voff, lds_void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 4, (int)voff, 0, 0, 0);
+}
+
+// Bytes from the first byte of row 0 to the last byte of row n-1 of a head
+// whose rows are `rs` bytes apart and `row` bytes long (0 for no rows); the
+// extent of the buffer resource over that head, so rows >= n read as zero.
+__device__ __forceinline__ uint32_t head_span(int n, uint32_t rs, uint32_t row) {
+  return n > 0 ? (uint32_t)(n - 1) * rs + row : 0u;
+}
+
+// One batch entry's query and key lengths and first packed rows. Without
+// packed sequences (cu_q null) every entry has the launch's lengths. Packed
+// offsets are clamped into [0, total] and the lengths to the launch's longest
+// ones, so a malformed offset array cannot move an access outside the tensors.
+struct Seq {
+  int nq, nk, tq, tk;
+};
+__device__ __forceinline__ Seq seq_of(const int* cu_q, const int* cu_k, int b, int Nq, int Nk, int total_q,
+                                      int total_k) {
+  if (!cu_q) return {Nq, Nk, 0, 0};
+  const int q0 = min(max(cu_q[b], 0), total_q), k0 = min(max(cu_k[b], 0), total_k);
+  const int q1 = min(max(cu_q[b + 1], q0), total_q), k1 = min(max(cu_k[b + 1], k0), total_k);
+  return {min(q1 - q0, Nq), min(k1 - k0, Nk), q0, k0};
 }
 
 // Transposing 8-byte LDS read of 16-bit elements (gfx950). Within each group
@@ -214,12 +241,58 @@ __device__ __forceinline__ void wg_map(int n_tiles, bool causal, int group, int&
   }
 }
 
-// K/V head of query head bh (over B*hq heads) when `group` query heads share
-// one K/V head: batch entry bh / hq, K/V head (bh % hq) / group of hq / group.
-__device__ __forceinline__ int kv_head(int bh, int hq, int group) {
-  if (group == 1) return bh;
-  return (bh / hq) * (hq / group) + (bh % hq) / group;
+// Offsets of the LDS-DMA loads that fill a row-major tile of two tensors
+// with the same tile shape (K and V, or Q and dO) whose rows are `ars` and
+// `brs` bytes apart in memory. Slot i of a lane (1 KB block wave*LPW + i of the
+// tile) reads tile row row0 + i * (1024 / RB) at chunk ch_i, so the second
+// tensor's offset is the first one's plus row * (brs - ars) (32-bit modular
+// arithmetic): one register per slot and one per lane serve both tensors.
+template <int RB, int LPW, int NW>
+__device__ __forceinline__ constexpr bool tile_rows_affine_ok() {
+  for (int w = 0; w < NW; ++w)
+    for (int lane = 0; lane < 64; ++lane) {
+      int r0 = 0, c0 = 0;
+      tile_pos<RB>(w * LPW * 64 + lane, r0, c0);
+      for (int i = 0; i < LPW; ++i) {
+        int r = 0, c = 0;
+        tile_pos<RB>((w * LPW + i) * 64 + lane, r, c);
+        if (r != r0 + i * (1024 / RB)) return false;
+      }
+    }
+  return true;
 }
+
+template <int LPW, int RB>
+struct TileLoader {
+  static_assert(1024 % RB == 0, "a 1 KB block holds whole rows");
+  uint32_t off[LPW];  // row_i * ars + 16 * ch_i
+  uint32_t dlt;       // row0 * (brs - ars)
+  uint32_t ars, brs;
+  __device__ __forceinline__ TileLoader(int wave, int lane, uint32_t ars_, uint32_t brs_) : ars(ars_), brs(brs_) {
+    dlt = 0;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      int row, ch;
+      tile_pos<RB>((wave * LPW + i) * 64 + lane, row, ch);
+      off[i] = (uint32_t)row * ars + (uint32_t)ch * 16;
+      if (i == 0) dlt = (uint32_t)row * (brs - ars);
+    }
+  }
+  // Byte offset of slot i of the first (a) or second (b) tensor for a tile
+  // starting at row r0. opaque() keeps the compiler from hoisting per-slot sums
+  // out of the tile loop into extra registers (one add per load is cheaper).
+  __device__ __forceinline__ uint32_t a(int i, int r0) const {
+    uint32_t o = off[i];
+    opaque(o);
+    return o + (uint32_t)r0 * ars;
+  }
+  __device__ __forceinline__ uint32_t b(int i, int r0) const {
+    uint32_t o = off[i], d = dlt;
+    opaque(o);
+    opaque(d);
+    return o + d + ((uint32_t)r0 * brs + (uint32_t)(i * (1024 / RB)) * (brs - ars));
+  }
+};
 
 // Keys that query row i keeps: key_lo(i) <= j <= key_hi(i). The causal
 // diagonal of row i is key i + (nk - nq), so the last query row lines up with
@@ -234,6 +307,15 @@ struct KeyBounds {
   // Queries that key row j is kept by: qlo(j) <= i <= qhi(j).
   __device__ __forceinline__ int qlo(int j) const { return causal ? max(0, j - (nk - nq)) : 0; }
   __device__ __forceinline__ int qhi(int j) const { return window >= 0 ? min(nq - 1, j - (nk - nq) + window) : nq - 1; }
+  // Does the key tile [key0, key0 + bn) need masking for the 32 query rows qw .. qw + 31 (ragged
+  // tail, causal diagonal or window start)? The terms are combined without short-circuit
+  // evaluation: a chain of branches placed right after an MFMA chain gave the compiler a join
+  // block reached by two paths, and on the shorter one it left too few wait states before the
+  // VALU read of the MFMA result (stale accumulator values for the fp32 D = 256 forward).
+  template <int BN>
+  __device__ __forceinline__ bool mask_tile(int key0, int qw) const {
+    return (key0 + BN > nk) | ((causal != 0) & (key0 + BN - 1 > hi(qw))) | ((window >= 0) & (key0 < lo(qw + 31)));
+  }
 };
 
 // vmcnt(0): all of this wave's vector-memory operations (incl. LDS DMA) done.

@@ -69,21 +69,19 @@ fwd_kernel(FwdParams P) {
   // tiles carry the most key tiles, so rank 0 is the last one.
   int bh, qt;
   wg_map(P.n_qtiles, P.causal, P.group, bh, qt);
-  if (P.causal) qt = P.n_qtiles - 1 - qt;
-  const int N = P.N;
+  const HeadRows hr = head_rows<C::ESZ>(P, bh);
+  const int N = hr.nq;
+  const int n_qt = (N + C::BM - 1) / C::BM;  // this entry's query tiles (fewer for a short packed sequence)
+  if (P.causal) qt = n_qt - 1 - qt;
+  if (qt < 0 || qt >= n_qt) return;  // whole workgroup: nothing of this entry is left
   const int q0 = qt * C::BM;
   const int qw = q0 + 32 * wave;
   const int qrow = qw + li;
 
-  const KeyBounds kb{N, P.Nk, P.causal, P.window};
-  const size_t head_elems = (size_t)N * D, kv_elems = (size_t)P.Nk * D;
-  const char* qh = reinterpret_cast<const char*>(P.q) + (size_t)bh * head_elems * C::ESZ;
-  const int kvh = kv_head(bh, P.hq, P.group);
-  const char* kh = reinterpret_cast<const char*>(P.k) + (size_t)kvh * kv_elems * C::ESZ;
-  const char* vh = reinterpret_cast<const char*>(P.v) + (size_t)kvh * kv_elems * C::ESZ;
-  const auto rq = make_rsrc(qh, (uint32_t)(head_elems * C::ESZ));
-  const auto rk = make_rsrc(kh, (uint32_t)(kv_elems * C::ESZ));
-  const auto rv = make_rsrc(vh, (uint32_t)(kv_elems * C::ESZ));
+  const KeyBounds kb{N, hr.nk, P.causal, P.window};
+  const auto rq = make_rsrc(hr.q, head_span(N, hr.qrs, RB));
+  const auto rk = make_rsrc(hr.k, head_span(hr.nk, hr.krs, RB));
+  const auto rv = make_rsrc(hr.v, head_span(hr.nk, hr.vrs, RB));
   float sc = P.scale_log2;
   float tau = P.rescale_log2;
   float out_mul = 1.f;
@@ -99,27 +97,21 @@ fwd_kernel(FwdParams P) {
   }
 
   // Loader: 16-byte slot `lane` of 1 KB block m of a tile comes from tile_pos(slot).
-  uint32_t goff[C::LPW];
-#pragma unroll
-  for (int i = 0; i < C::LPW; ++i) {
-    int row, ch;
-    tile_pos<RB>((wave * C::LPW + i) * 64 + lane, row, ch);
-    goff[i] = (uint32_t)(row * RB + ch * 16);
-  }
+  static_assert(tile_rows_affine_ok<RB, C::LPW, C::NW>(), "loader rows");
+  const TileLoader<C::LPW, RB> tl(wave, lane, hr.krs, hr.vrs);
   auto issue = [&](int key0, char* dst) {
-    const uint32_t base = (uint32_t)key0 * RB;
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i) {
       const int m = wave * C::LPW + i;
-      buf_load_lds16(rk, goff[i] + base, 0, (lds_void*)(dst + m * 1024));
-      buf_load_lds16(rv, goff[i] + base, 0, (lds_void*)(dst + C::TILE + m * 1024));
+      buf_load_lds16(rk, tl.a(i, key0), 0, (lds_void*)(dst + m * 1024));
+      buf_load_lds16(rv, tl.b(i, key0), 0, (lds_void*)(dst + C::TILE + m * 1024));
     }
   };
 
   // Q^T pieces (B operand of S^T = K Q^T): lane-half h holds bytes 32p + 16h.
   i32x4 qf[NP];
 #pragma unroll
-  for (int p = 0; p < NP; ++p) qf[p] = buf_load16(rq, (uint32_t)qrow * RB + 32 * p + 16 * hf);
+  for (int p = 0; p < NP; ++p) qf[p] = buf_load16(rq, (uint32_t)qrow * hr.qrs + 32 * p + 16 * hf);
 
   // Per-lane LDS read offsets (tile-relative); blocks and key chunks add whole rows.
   uint32_t koff[NP];
@@ -214,7 +206,7 @@ fwd_kernel(FwdParams P) {
         }
       }
       // ---- mask (causal diagonal, window start, ragged tail) and tile row max ----
-      if ((key0 + BN > kb.nk) || (P.causal && key0 + BN - 1 > kb.hi(qw)) || (kb.window >= 0 && key0 < kb.lo(qw + 31))) {
+      if (kb.mask_tile<BN>(key0, qw)) {
         // key key0 + 32b + 8(v/4) + 4h + v%4 is kept iff key_lo(qrow) <= key <= key_hi(qrow);
         // compare the lane-independent part r against two per-lane limits.
         const int hi = kb.hi(qrow) - key0 - 4 * hf, lo = kb.lo(qrow) - key0 - 4 * hf;
@@ -332,25 +324,31 @@ fwd_kernel(FwdParams P) {
   }
 
   // ---- epilogue: O = acc / l, lse = ln(sum exp(s)) ----
+  // A row that kept no key has l = 0 and m_ref = -inf: O = 0 and lse = -inf.
   const float l_tot = pair_sum32(l_part);
-  const float inv = out_mul / l_tot;
+  const float inv = l_tot > 0.f ? out_mul / l_tot : 0.f;
   if (qrow < N) {
-    const size_t row_base = ((size_t)bh * N + qrow) * D;
+    if constexpr (C::elt == Elt::F32) {
+      float* orow = reinterpret_cast<float*>(hr.o) + (size_t)qrow * P.so.r;
 #pragma unroll
-    for (int e = 0; e < NE; ++e)
+      for (int e = 0; e < NE; ++e)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = 32 * e + 8 * g + 4 * hf;
-        if constexpr (C::elt == Elt::F32) {
+        for (int g = 0; g < 4; ++g) {
           f32x4 o4 = {acc[e][4 * g] * inv, acc[e][4 * g + 1] * inv, acc[e][4 * g + 2] * inv, acc[e][4 * g + 3] * inv};
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(P.o) + row_base + d) = o4;
-        } else {
+          *reinterpret_cast<f32x4*>(orow + 32 * e + 8 * g + 4 * hf) = o4;
+        }
+    } else {
+      __bf16* orow = reinterpret_cast<__bf16*>(hr.o) + (size_t)qrow * P.so.r;
+#pragma unroll
+      for (int e = 0; e < NE; ++e)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
           bf16x4 o4 = {(__bf16)(acc[e][4 * g] * inv), (__bf16)(acc[e][4 * g + 1] * inv),
                        (__bf16)(acc[e][4 * g + 2] * inv), (__bf16)(acc[e][4 * g + 3] * inv)};
-          *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(P.o) + row_base + d) = o4;
+          *reinterpret_cast<bf16x4*>(orow + 32 * e + 8 * g + 4 * hf) = o4;
         }
-      }
-    if (hf == 0) P.lse[(size_t)bh * N + qrow] = (m_ref + __builtin_log2f(l_tot)) * kLn2;
+    }
+    if (hf == 0) hr.lse[qrow] = (m_ref + __builtin_log2f(l_tot)) * kLn2;
   }
 }
 
@@ -386,29 +384,24 @@ fwd_pipe_kernel(FwdParams P) {
 
   int bh, qt;
   wg_map(P.n_qtiles, P.causal, P.group, bh, qt);
-  if (P.causal) qt = P.n_qtiles - 1 - qt;
-  const int N = P.N;
+  const HeadRows hr = head_rows<2>(P, bh);
+  const int N = hr.nq;
+  const int n_qt = (N + C::BM - 1) / C::BM;
+  if (P.causal) qt = n_qt - 1 - qt;
+  if (qt < 0 || qt >= n_qt) return;
   const int q0 = qt * C::BM;
   const int qw = q0 + 32 * wave;
   const int qrow = qw + li;
 
-  const KeyBounds kb{N, P.Nk, P.causal, P.window};
-  const size_t head_elems = (size_t)N * D, kv_elems = (size_t)P.Nk * D;
-  const auto rq = make_rsrc(reinterpret_cast<const char*>(P.q) + (size_t)bh * head_elems * 2,
-                            (uint32_t)(head_elems * 2));
-  const int kvh = kv_head(bh, P.hq, P.group);
-  const auto rk = make_rsrc(reinterpret_cast<const char*>(P.k) + (size_t)kvh * kv_elems * 2, (uint32_t)(kv_elems * 2));
-  const auto rv = make_rsrc(reinterpret_cast<const char*>(P.v) + (size_t)kvh * kv_elems * 2, (uint32_t)(kv_elems * 2));
+  const KeyBounds kb{N, hr.nk, P.causal, P.window};
+  const auto rq = make_rsrc(hr.q, head_span(N, hr.qrs, RB));
+  const auto rk = make_rsrc(hr.k, head_span(hr.nk, hr.krs, RB));
+  const auto rv = make_rsrc(hr.v, head_span(hr.nk, hr.vrs, RB));
   const float sc = P.scale_log2;
   const float tau = P.rescale_log2;
 
-  uint32_t goff[C::LPW];
-#pragma unroll
-  for (int i = 0; i < C::LPW; ++i) {
-    int row, ch;
-    tile_pos<RB>((wave * C::LPW + i) * 64 + lane, row, ch);
-    goff[i] = (uint32_t)(row * RB + ch * 16);
-  }
+  static_assert(tile_rows_affine_ok<RB, C::LPW, C::NW>(), "loader rows");
+  const TileLoader<C::LPW, RB> tl(wave, lane, hr.krs, hr.vrs);
   // Key tiles t_lo + j, j = 0 .. n_tiles-1, cover the keys any row of the
   // workgroup keeps; t counts from t_lo below.
   const int t_lo = kb.lo(q0) / BN;
@@ -417,16 +410,21 @@ fwd_pipe_kernel(FwdParams P) {
   // whose window starts later see fully masked tiles first, which add nothing)
   const int n_live = min(n_tiles, kb.hi(qw + 31) / BN + 1 - t_lo);
 
-  auto issue = [&](const __amdgpu_buffer_rsrc_t& r, int t, char* dst) {
-    const uint32_t base = (uint32_t)((t_lo + t) * BN) * RB;
+  // K tile t (counted from t_lo) into dst; V tile t into dst
+  auto issue_k = [&](int t, char* dst) {
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i)
-      buf_load_lds16(r, goff[i] + base, 0, (lds_void*)(dst + (wave * C::LPW + i) * 1024));
+      buf_load_lds16(rk, tl.a(i, (t_lo + t) * BN), 0, (lds_void*)(dst + (wave * C::LPW + i) * 1024));
+  };
+  auto issue_v = [&](int t, char* dst) {
+#pragma unroll
+    for (int i = 0; i < C::LPW; ++i)
+      buf_load_lds16(rv, tl.b(i, (t_lo + t) * BN), 0, (lds_void*)(dst + (wave * C::LPW + i) * 1024));
   };
 
   i32x4 qf[NP];
 #pragma unroll
-  for (int p = 0; p < NP; ++p) qf[p] = buf_load16(rq, (uint32_t)qrow * RB + 32 * p + 16 * hf);
+  for (int p = 0; p < NP; ++p) qf[p] = buf_load16(rq, (uint32_t)qrow * hr.qrs + 32 * p + 16 * hf);
 
   static_assert(piece_xor_ok<RB, NP>() && tr16_xor_ok<RB, true, NE>(), "offset XOR form");
   uint32_t kbase = tile_off<RB>(li, hf);
@@ -517,7 +515,7 @@ fwd_pipe_kernel(FwdParams P) {
     if (with_max && use_max) {
       // key key0 + 4h + r of tile t (r = 32b + 8(v/4) + v%4) is kept iff lo <= r <= hi
       const int key0 = (t_lo + t) * BN;
-      if ((key0 + BN > kb.nk) || (P.causal && key0 + BN - 1 > kb.hi(qw)) || (kb.window >= 0 && key0 < kb.lo(qw + 31))) {
+      if (kb.mask_tile<BN>(key0, qw)) {
         int hi = kb.hi(qrow) - key0 - 4 * hf, lo = kb.lo(qrow) - key0 - 4 * hf;
         opaque(hi);
         opaque(lo);
@@ -579,9 +577,9 @@ fwd_pipe_kernel(FwdParams P) {
   };
 
   // ---- prologue: K_0, V_0, K_1 in; S_0 and its max ----
-  issue(rk, 0, kb0);
-  issue(rv, 0, vb0);
-  if (n_tiles > 1) issue(rk, 1, kb1);
+  issue_k(0, kb0);
+  issue_v(0, vb0);
+  if (n_tiles > 1) issue_k(1, kb1);
   wait_vmem();
   __syncthreads();
   if (n_live > 0) {
@@ -593,8 +591,8 @@ fwd_pipe_kernel(FwdParams P) {
   // One iteration; sc_ holds S_j on entry, sn_ receives S_{j+1}.
   auto iter = [&](int j, const char* __restrict__ kcur, const char* __restrict__ vcur, char* __restrict__ knxt,
                   char* __restrict__ vnxt, f32x16 (&sc_)[NB], f32x16 (&sn_)[NB]) __attribute__((always_inline)) {
-    if (j + 1 < n_tiles) issue(rv, j + 1, vnxt);
-    if (j + 2 < n_tiles) issue(rk, j + 2, knxt);
+    if (j + 1 < n_tiles) issue_v(j + 1, vnxt);
+    if (j + 2 < n_tiles) issue_k(j + 2, knxt);
     opaque(kbase);
     opaque(vbase);
     if (j < n_live) {
@@ -610,21 +608,20 @@ fwd_pipe_kernel(FwdParams P) {
     if (j + 1 < n_tiles) iter(j + 1, kb0, vb1, kb1, vb0, sb, sa);
   }
 
-  // ---- epilogue: O = acc / l, lse = ln(sum exp(s)) ----
+  // ---- epilogue: O = acc / l, lse = ln(sum exp(s)); O = 0, lse = -inf for a row that kept no key ----
   const float l_tot = pair_sum32(l_part);
-  const float inv = 1.f / l_tot;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qrow < N) {
-    const size_t row_base = ((size_t)bh * N + qrow) * D;
+    __bf16* orow = reinterpret_cast<__bf16*>(hr.o) + (size_t)qrow * P.so.r;
 #pragma unroll
     for (int e = 0; e < NE; ++e)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d = 32 * e + 8 * g + 4 * hf;
         bf16x4 o4 = {(__bf16)(acc[e][4 * g] * inv), (__bf16)(acc[e][4 * g + 1] * inv),
                      (__bf16)(acc[e][4 * g + 2] * inv), (__bf16)(acc[e][4 * g + 3] * inv)};
-        *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(P.o) + row_base + d) = o4;
+        *reinterpret_cast<bf16x4*>(orow + 32 * e + 8 * g + 4 * hf) = o4;
       }
-    if (hf == 0) P.lse[(size_t)bh * N + qrow] = (m_ref + __builtin_log2f(l_tot)) * kLn2;
+    if (hf == 0) hr.lse[qrow] = (m_ref + __builtin_log2f(l_tot)) * kLn2;
   }
 }
 

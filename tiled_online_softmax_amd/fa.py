@@ -21,9 +21,9 @@ FA_F32, FA_BF16, FA_FP8_E4M3 = 0, 1, 2
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, 1, 2, 3, 4
 FA_BWD_ATOMIC, FA_BWD_DETERMINISTIC = 0, 1
 
-EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_general", "fa_fwd_ex", "fa_fwd_fp8", "fa_quantize_fp8",
-            "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_gqa", "fa_bwd_general", "fa_bwd_dkdv", "fa_status_string",
-            "fa_last_error")
+EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_general", "fa_fwd_strided", "fa_fwd_varlen", "fa_fwd_ex", "fa_fwd_fp8",
+            "fa_quantize_fp8", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_gqa", "fa_bwd_general", "fa_bwd_strided",
+            "fa_bwd_varlen", "fa_bwd_dkdv", "fa_status_string", "fa_last_error")
 
 
 class FAError(RuntimeError):
@@ -46,6 +46,8 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd.argtypes = [_vp] * 5 + [_i] * 5 + [_f, _i, _vp]
         L.fa_fwd_gqa.argtypes = [_vp] * 5 + [_i] * 6 + [_f, _i, _vp]
         L.fa_fwd_general.argtypes = [_vp] * 5 + [_i] * 8 + [_f, _i, _vp]
+        L.fa_fwd_strided.argtypes = [_vp] * 5 + [_i] * 8 + [_f, _i, _vp, _vp]
+        L.fa_fwd_varlen.argtypes = [_vp] * 7 + [_i] * 10 + [_f, _i, _vp]
         L.fa_fwd_ex.argtypes = [_vp] * 5 + [_i] * 5 + [_f, _i, _f, _vp]
         L.fa_fwd_fp8.argtypes = [_vp] * 5 + [_i] * 5 + [_f] + [_vp] * 3 + [_vp]
         L.fa_quantize_fp8.argtypes = [_vp, _sz, _vp, _vp, _vp]
@@ -54,13 +56,16 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd.argtypes = [_vp] * 9 + [_i] * 5 + [_f, _i, _i, _vp, _sz, _vp]
         L.fa_bwd_gqa.argtypes = [_vp] * 9 + [_i] * 6 + [_f, _i, _i, _vp, _sz, _vp]
         L.fa_bwd_general.argtypes = [_vp] * 9 + [_i] * 8 + [_f, _i, _i, _vp, _sz, _vp]
+        L.fa_bwd_strided.argtypes = [_vp] * 9 + [_i] * 8 + [_f, _i, _i, _vp, _sz, _vp, _vp]
+        L.fa_bwd_varlen.argtypes = [_vp] * 11 + [_i] * 10 + [_f, _i, _i, _vp, _sz, _vp]
         L.fa_bwd_dkdv.argtypes = [_vp] * 8 + [_i] * 5 + [_f, _i, _vp, _sz, _vp]
         L.fa_status_string.argtypes = [_i]
         L.fa_status_string.restype = ctypes.c_char_p
         L.fa_last_error.argtypes = []
         L.fa_last_error.restype = ctypes.c_char_p
-        for name in ("fa_fwd", "fa_fwd_gqa", "fa_fwd_general", "fa_fwd_ex", "fa_fwd_fp8", "fa_quantize_fp8", "fa_bwd",
-                     "fa_bwd_gqa", "fa_bwd_general", "fa_bwd_dkdv"):
+        for name in ("fa_fwd", "fa_fwd_gqa", "fa_fwd_general", "fa_fwd_strided", "fa_fwd_varlen", "fa_fwd_ex",
+                     "fa_fwd_fp8", "fa_quantize_fp8", "fa_bwd", "fa_bwd_gqa", "fa_bwd_general", "fa_bwd_strided",
+                     "fa_bwd_varlen", "fa_bwd_dkdv"):
             getattr(L, name).restype = _i
         _lib = L
     return _lib
@@ -93,9 +98,9 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def _check_qkv(*ts: torch.Tensor, kv=(), same_len=True):
+def _check_qkv(*ts: torch.Tensor, kv=(), same_len=True, dense=True):
     """q-shaped tensors `ts` and K/V-shaped tensors `kv` (same B and D, H a multiple of their head count,
-    and the same length unless `same_len` is False)."""
+    and the same length unless `same_len` is False); contiguous, or with only D contiguous if not `dense`."""
     ref = ts[0]
     if ref.dim() != 4:
         raise ValueError("tensors must be [B, H, N, D]")
@@ -104,8 +109,10 @@ def _check_qkv(*ts: torch.Tensor, kv=(), same_len=True):
             raise ValueError("tensors must be on a GPU device")
         if t.dtype != ref.dtype or t.device != ref.device:
             raise ValueError("tensors must share dtype and device")
-        if not t.is_contiguous():
+        if dense and not t.is_contiguous():
             raise ValueError("tensors must be contiguous [B, H, N, D]")
+        if not dense and t.stride(-1) != 1:
+            raise ValueError("the head dimension D must be contiguous")
     for t in ts:
         if t.shape != ref.shape:
             raise ValueError("q-shaped tensors must share one shape")
@@ -121,6 +128,18 @@ def _check_qkv(*ts: torch.Tensor, kv=(), same_len=True):
             raise ValueError("k/v must have as many rows as q here")
 
 
+def _strides(*ts: torch.Tensor, lse: torch.Tensor):
+    """Host array of element strides: (batch, head, row) of each [B, H, N, D] tensor, then lse (batch, head)."""
+    if lse.stride(2) != 1:
+        raise ValueError("lse rows must be contiguous")
+    vals = [x for t in ts for x in t.stride()[:3]] + list(lse.stride()[:2])
+    return (ctypes.c_longlong * len(vals))(*vals)
+
+
+def _dense(*ts) -> bool:
+    return all(t is None or t.is_contiguous() for t in ts)
+
+
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False, scale: Optional[float] = None,
         rescale_log2: Optional[float] = None, out: Optional[torch.Tensor] = None,
         lse: Optional[torch.Tensor] = None, window: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
@@ -128,8 +147,11 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
 
     k, v may have fewer heads (grouped-query) and a different length than q (causal is then
     aligned at the bottom right); `window` (>= 0) keeps only the keys from i + Nk - Nq - window on.
+    Tensors may be any [B, H, N, D] views with D contiguous (e.g. x.view(B, N, H, D).transpose(1, 2));
+    non-contiguous ones go through fa_fwd_strided.
     """
-    _check_qkv(q, kv=(k, v), same_len=False)
+    dense = _dense(q, k, v, out, lse)
+    _check_qkv(q, kv=(k, v), same_len=False, dense=dense)
     B, H, N, D = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
     code = _dtype_code(q)
@@ -138,6 +160,15 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
         out = torch.empty(q.shape, dtype=torch.float32 if code == FA_F32 else torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if not dense:
+        if rescale_log2 is not None:
+            raise ValueError("rescale_log2 is only taken with contiguous tensors")
+        if out.shape != q.shape or lse.shape != (B, H, N):
+            raise ValueError("out must be shaped like q and lse [B, H, N]")
+        _check(lib().fa_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,
+                                    Hkv, N, Nk, D, int(causal), -1 if window is None else int(window), scale, code,
+                                    _strides(q, k, v, out, lse=lse), _stream(q)))
+        return out, lse
     if Nk != N or window is not None:
         if rescale_log2 is not None:
             raise ValueError("rescale_log2 is only taken with equal lengths and no window")
@@ -201,19 +232,32 @@ def bwd_workspace_size(B: int, H: int, N: int, D: int, variant: int = FA_BWD_ATO
 
 def bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None, variant: int = FA_BWD_ATOMIC,
         workspace: Optional[torch.Tensor] = None, dq=None, dk=None, dv=None, window: Optional[int] = None):
-    """Attention backward (bf16). Returns (dQ, dK, dV) as bf16 tensors; dK, dV have k's shape."""
-    _check_qkv(q, o, do, kv=(k, v), same_len=False)
+    """Attention backward (bf16). Returns (dQ, dK, dV) as bf16 tensors; dK, dV have k's shape.
+
+    Non-contiguous [B, H, N, D] views (D contiguous) go through fa_bwd_strided."""
+    dense = _dense(q, k, v, o, do, dq, dk, dv, lse)
+    _check_qkv(q, o, do, kv=(k, v), same_len=False, dense=dense)
     B, H, N, D = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    if lse.dtype != torch.float32 or lse.shape != (B, H, N) or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 [B, H, N]")
+    if lse.dtype != torch.float32 or lse.shape != (B, H, N):
+        raise ValueError("lse must be float32 [B, H, N]")
     need = bwd_workspace_size(B, H, N, D, variant)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    dq = torch.empty(q.shape, dtype=q.dtype, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=k.dtype, device=k.device) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=v.dtype, device=v.device) if dv is None else dv
+    if not dense:
+        for t, like in ((dq, q), (dk, k), (dv, v)):
+            if t.shape != like.shape or t.stride(-1) != 1:
+                raise ValueError("gradients must be shaped like their inputs with D contiguous")
+        _check(lib().fa_bwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                    lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, Nk, D,
+                                    int(causal), -1 if window is None else int(window), scale, _dtype_code(q),
+                                    variant, workspace.data_ptr(), workspace.numel(),
+                                    _strides(q, k, v, o, do, dq, dk, dv, lse=lse), _stream(q)))
+        return dq, dk, dv
     if Nk != N or window is not None:
         _check(lib().fa_bwd_general(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
                                     lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, Nk, D,
@@ -249,3 +293,57 @@ def bwd_dkdv(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] =
                              dk.data_ptr(), dv.data_ptr(), B, H, N, D, int(causal), scale, _dtype_code(q),
                              workspace.data_ptr(), workspace.numel(), _stream(q)))
     return dk, dv
+
+
+def _check_varlen(q, k, v, cu_q, cu_k):
+    for t in (q, k, v):
+        if t.dim() != 3 or not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError("packed tensors must be contiguous [total, heads, D] device tensors of one dtype")
+    if k.shape != v.shape or k.shape[2] != q.shape[2] or q.shape[1] % k.shape[1]:
+        raise ValueError("k, v must be [total_k, Hkv, D] with Hkv dividing q's heads")
+    for c in (cu_q, cu_k):
+        if c.dtype != torch.int32 or not c.is_cuda or not c.is_contiguous() or c.dim() != 1:
+            raise ValueError("cu_seqlens must be contiguous int32 device tensors")
+    if cu_q.numel() != cu_k.numel() or cu_q.numel() < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both have B + 1 >= 2 entries")
+
+
+def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int, causal: bool = False,
+               scale: Optional[float] = None, window: Optional[int] = None, out=None, lse=None):
+    """Packed variable-length forward: q [total_q, H, D], k, v [total_k, Hkv, D], int32 offsets [B + 1].
+    Returns (O [total_q, H, D], lse [H, total_q])."""
+    _check_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    Tq, H, D = q.shape
+    Tk, Hkv = k.shape[0], k.shape[1]
+    B = cu_seqlens_q.numel() - 1
+    code = _dtype_code(q)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    out = torch.empty(q.shape, dtype=torch.float32 if code == FA_F32 else torch.bfloat16, device=q.device) \
+        if out is None else out
+    lse = torch.empty((H, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(lib().fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                               cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H, Hkv, Tq, Tk,
+                               int(max_seqlen_q), int(max_seqlen_k), D, int(causal),
+                               -1 if window is None else int(window), scale, code, _stream(q)))
+    return out, lse
+
+
+def bwd_varlen(q, k, v, o, do, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+               causal: bool = False, scale: Optional[float] = None, window: Optional[int] = None,
+               variant: int = FA_BWD_ATOMIC, workspace=None):
+    """Gradients of fwd_varlen (bf16). Returns (dQ, dK, dV) in the packed layouts."""
+    _check_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    Tq, H, D = q.shape
+    Tk, Hkv = k.shape[0], k.shape[1]
+    B = cu_seqlens_q.numel() - 1
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    need = bwd_workspace_size(1, H, Tq, D, variant)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.zeros_like(k), torch.zeros_like(v)
+    _check(lib().fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                               dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cu_seqlens_q.data_ptr(),
+                               cu_seqlens_k.data_ptr(), B, H, Hkv, Tq, Tk, int(max_seqlen_q), int(max_seqlen_k), D,
+                               int(causal), -1 if window is None else int(window), scale, _dtype_code(q), variant,
+                               workspace.data_ptr(), workspace.numel(), _stream(q)))
+    return dq, dk, dv
