@@ -40,15 +40,15 @@ constexpr float kInf = __builtin_huge_valf();
 // same row as cu_q[b] + i of entry b). A row that kept no key (lse = -inf)
 // gets +inf, so every recomputed probability of it is 2^-inf = 0.
 // ---------------------------------------------------------------------------
+// Grid: `nb` blocks of 256 / TPR rows per head, for each of the Bp * H heads in turn.
 template <int D>
-__global__ void __launch_bounds__(256) bwd_pre_kernel(BwdParams P, int H, int Np) {
+__global__ void __launch_bounds__(256) bwd_pre_kernel(BwdParams P, int H, int Np, int nb) {
   constexpr int TPR = D / 8;  // threads per row
-  const long long gt = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long row = gt / TPR;
-  const int part = (int)(gt % TPR);
-  const bool in = row < P.rows;
-  const int r = in ? (int)row : 0;  // rows < 2^29
-  const int i = r % Np, bh = r / Np, h = bh % H, b = bh / H;
+  const int bh = (int)blockIdx.x / nb, h = bh % H, b = bh / H;  // wave-uniform
+  const int i = ((int)blockIdx.x - bh * nb) * (256 / TPR) + (int)threadIdx.x / TPR;
+  const int part = (int)threadIdx.x % TPR;
+  const bool in = i < Np;
+  const long long row = (long long)bh * Np + i;
   float s = 0.f;
   if (in) {
     const __bf16* o = static_cast<const __bf16*>(P.o) + (b * P.so.b + h * P.so.h + i * P.so.r) + part * 8;
@@ -72,16 +72,15 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(BwdParams P, int H, int Np
   }
 }
 
-// dQ = bf16(dQ_accum) (the scale is already applied); rows as in bwd_pre_kernel.
+// dQ = bf16(dQ_accum) (the scale is already applied); rows and grid as in bwd_pre_kernel.
 template <int D>
-__global__ void __launch_bounds__(256) bwd_dq_convert_kernel(BwdParams P, int H, int Np) {
+__global__ void __launch_bounds__(256) bwd_dq_convert_kernel(BwdParams P, int H, int Np, int nb) {
   constexpr int TPR = D / 8;
-  const long long gt = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long row = gt / TPR;
-  if (row >= P.rows) return;
-  const int part = (int)(gt % TPR);
-  const int r = (int)row;
-  const int i = r % Np, bh = r / Np, h = bh % H, b = bh / H;
+  const int bh = (int)blockIdx.x / nb, h = bh % H, b = bh / H;
+  const int i = ((int)blockIdx.x - bh * nb) * (256 / TPR) + (int)threadIdx.x / TPR;
+  if (i >= Np) return;
+  const int part = (int)threadIdx.x % TPR;
+  const long long row = (long long)bh * Np + i;
   const f32x4 a = *reinterpret_cast<const f32x4*>(P.dq_accum + row * D + part * 8);
   const f32x4 c = *reinterpret_cast<const f32x4*>(P.dq_accum + row * D + part * 8 + 4);
   bf16x8 v;
@@ -117,7 +116,10 @@ struct DkdvCfg {
   static_assert(RB_DS == 64 || RB_DS == 128 || RB_DS % 256 == 0, "dS tile row");
 };
 
-template <class C, bool ATOMIC>
+// PLAIN: Q and dO rows are equally spaced and every query tile's workspace
+// rows start at a multiple of 4 (fixed lengths with Nq % 4 == 0), so one loader
+// offset serves Q and dO and the per-row values arrive in 16-byte pieces.
+template <class C, bool ATOMIC, bool PLAIN>
 __global__ void __launch_bounds__(C::NT)
 __attribute__((amdgpu_waves_per_eu(C::OCC, C::OCC)))
 bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
@@ -174,7 +176,7 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
   }
 
   static_assert(tile_rows_affine_ok<RB, C::LPW, C::NW>(), "loader rows");
-  const TileLoader<C::LPW, RB> tl(wave, lane, qrs, dors);
+  TileLoader<C::LPW, RB, PLAIN> tl(wave, lane, qrs, dors);
   // Query tile of head g of the group starting at query i0.
   auto issue = [&](int g, int i0, char* st) {
 #pragma unroll
@@ -183,11 +185,20 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
       buf_load_lds16(rq, tl.a(i, i0) + (uint32_t)g * qhs, 0, (lds_void*)(st + m * 1024));
       buf_load_lds16(rdo, tl.b(i, i0) + (uint32_t)g * dohs, 0, (lds_void*)(st + C::OFF_DO + m * 1024));
     }
-    // lanes 0..BQ-1 (of the first 2*BQ/64 waves) bring lse*log2e of the tile's rows, lanes BQ..2BQ-1 their -D
-    if (wave < 2 * BQ / 64) {
-      const int L = wave * 64 + lane, half = L >= BQ, j = L - half * BQ;
-      const uint32_t r = ld_row0 + (uint32_t)g * ld_h + (uint32_t)(i0 + j);
-      buf_load_lds4(rld, (half ? ld_nd : 0u) + 4 * r, (lds_void*)(st + C::OFF_LD + wave * 256));
+    if constexpr (PLAIN) {
+      // lanes 0..BQ/4-1 bring lse*log2e of the tile's rows (4 per lane), the next BQ/4 lanes their -D
+      if (wave == 0 && lane < BQ / 2) {
+        const int half = lane >= BQ / 4, j = lane - half * (BQ / 4);
+        const uint32_t r = ld_row0 + (uint32_t)g * ld_h + (uint32_t)i0;
+        buf_load_lds16(rld, (half ? ld_nd : 0u) + 4 * r + 16 * j, 0, (lds_void*)(st + C::OFF_LD));
+      }
+    } else {
+      // lanes 0..BQ-1 (of the first 2*BQ/64 waves) bring lse*log2e of the tile's rows, lanes BQ..2BQ-1 their -D
+      if (wave < 2 * BQ / 64) {
+        const int L = wave * 64 + lane, half = L >= BQ, j = L - half * BQ;
+        const uint32_t r = ld_row0 + (uint32_t)g * ld_h + (uint32_t)(i0 + j);
+        buf_load_lds4(rld, (half ? ld_nd : 0u) + 4 * r, (lds_void*)(st + C::OFF_LD + wave * 256));
+      }
     }
   };
 
@@ -447,7 +458,8 @@ struct DqCfg {
   static_assert(TILE % (1024 * NW) == 0 && BN % 32 == 0, "tile shape");
 };
 
-template <class C>
+// SAME: K and V rows are equally spaced.
+template <class C, bool SAME>
 __global__ void __launch_bounds__(C::NT)
 __attribute__((amdgpu_waves_per_eu(C::OCC, C::OCC)))
 bwd_dq_kernel(BwdParams P, int n_qtiles) {
@@ -496,7 +508,7 @@ bwd_dq_kernel(BwdParams P, int n_qtiles) {
   const float sl2 = P.scale_log2;
 
   static_assert(tile_rows_affine_ok<RB, C::LPW, C::NW>(), "loader rows");
-  const TileLoader<C::LPW, RB> tl(wave, lane, krs, vrs);
+  TileLoader<C::LPW, RB, SAME> tl(wave, lane, krs, vrs);
   auto issue = [&](int key0, char* kb) {
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i) {
@@ -637,40 +649,59 @@ bwd_dq_kernel(BwdParams P, int n_qtiles) {
 
 // Workspace rows of the preprocess and the dQ convert: Bp entries of Np rows
 // per head (packed sequences: one entry of all packed rows).
+// Row blocks per head of the preprocess and dQ-convert grids.
+template <int D>
+static int row_blocks(int Np) {
+  constexpr int RPB = 256 / (D / 8);  // rows per block
+  return (Np + RPB - 1) / RPB;
+}
+
 template <int D>
 static hipError_t launch_pre(const BwdParams& p, int H, hipStream_t st) {
-  const long long threads = p.rows * (D / 8);
-  const int Np = p.cu_q ? p.total_q : p.N;
-  hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, p, H, Np);
+  const int Np = p.cu_q ? p.total_q : p.N, nb = row_blocks<D>(Np);
+  const long long grid = (long long)nb * (p.rows / Np);
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)grid), dim3(256), 0, st, p, H, Np, nb);
   return hipGetLastError();
 }
 
 template <class KCA, class KCD, class QC>
 static hipError_t launch_bwd(int variant, const BwdParams& p, int B, int H, hipStream_t st) {
   const int HKV = H / p.group;  // the key-tile passes run over K/V heads
+  // Q/dO equally spaced and workspace rows of every query tile 16-byte aligned
+  const bool plain = p.sq.r == p.sdo.r && !p.cu_q && p.N % 4 == 0;
   hipError_t e = launch_pre<KCD::D>(p, H, st);
   if (e != hipSuccess) return e;
   if (variant == 0) {
     const int nk = (p.Nk + KCA::BK - 1) / KCA::BK;
     const long long gk = (long long)nk * B * HKV;
     if (gk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<KCA, true>), dim3((unsigned)gk), dim3(KCA::NT), 0, st, p, nk);
+    if (plain)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<KCA, true, true>), dim3((unsigned)gk), dim3(KCA::NT), 0, st, p, nk);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<KCA, true, false>), dim3((unsigned)gk), dim3(KCA::NT), 0, st, p, nk);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const long long n8 = p.rows * KCA::D / 8;
-    const int Np = p.cu_q ? p.total_q : p.N;
-    hipLaunchKernelGGL(bwd_dq_convert_kernel<KCA::D>, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, p, H, Np);
+    const int Np = p.cu_q ? p.total_q : p.N, nb = row_blocks<KCA::D>(Np);
+    hipLaunchKernelGGL(bwd_dq_convert_kernel<KCA::D>, dim3((unsigned)((long long)nb * (p.rows / Np))), dim3(256), 0,
+                       st, p, H, Np, nb);
     return hipGetLastError();
   }
   const int nk = (p.Nk + KCD::BK - 1) / KCD::BK;
   const long long gk = (long long)nk * B * HKV;
   if (gk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<KCD, false>), dim3((unsigned)gk), dim3(KCD::NT), 0, st, p, nk);
+  if (plain)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<KCD, false, true>), dim3((unsigned)gk), dim3(KCD::NT), 0, st, p, nk);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<KCD, false, false>), dim3((unsigned)gk), dim3(KCD::NT), 0, st, p, nk);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (variant == 2) return hipSuccess;  // dK/dV only
   const int nq = (p.N + QC::BM - 1) / QC::BM;
   const long long gq = (long long)nq * B * H;
   if (gq > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(bwd_dq_kernel<QC>, dim3((unsigned)gq), dim3(QC::NT), 0, st, p, nq);
+  if (p.sk.r == p.sv.r)
+    hipLaunchKernelGGL((bwd_dq_kernel<QC, true>), dim3((unsigned)gq), dim3(QC::NT), 0, st, p, nq);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<QC, false>), dim3((unsigned)gq), dim3(QC::NT), 0, st, p, nq);
   return hipGetLastError();
 }
 

@@ -188,6 +188,11 @@ template <class T>
 __device__ __forceinline__ void opaque(T& x) {
   asm volatile("" : "+v"(x));
 }
+// The same for a wave-uniform value held in a scalar register.
+template <class T>
+__device__ __forceinline__ void opaque_s(T& x) {
+  asm volatile("" : "+s"(x));
+}
 
 // Transposing 8-byte LDS read of 8-bit elements (gfx950). Within each group
 // of 16 lanes, lane j supplies the address of 8 consecutive bytes M[j][0..7];
@@ -262,7 +267,9 @@ __device__ __forceinline__ constexpr bool tile_rows_affine_ok() {
   return true;
 }
 
-template <int LPW, int RB>
+// SAME: both tensors have the same row spacing (ars == brs); the second
+// tensor then uses the first one's offsets.
+template <int LPW, int RB, bool SAME>
 struct TileLoader {
   static_assert(1024 % RB == 0, "a 1 KB block holds whole rows");
   uint32_t off[LPW];  // row_i * ars + 16 * ch_i
@@ -275,22 +282,28 @@ struct TileLoader {
       int row, ch;
       tile_pos<RB>((wave * LPW + i) * 64 + lane, row, ch);
       off[i] = (uint32_t)row * ars + (uint32_t)ch * 16;
-      if (i == 0) dlt = (uint32_t)row * (brs - ars);
+      if (i == 0 && !SAME) dlt = (uint32_t)row * (brs - ars);
     }
   }
   // Byte offset of slot i of the first (a) or second (b) tensor for a tile
-  // starting at row r0. opaque() keeps the compiler from hoisting per-slot sums
-  // out of the tile loop into extra registers (one add per load is cheaper).
+  // starting at row r0. The tile's scalar base goes through opaque_s (and the
+  // per-lane delta through opaque, in place), so the compiler cannot split off
+  // a loop-invariant part of the sum and hoist per-slot partial sums out of the
+  // tile loop into registers of their own.
   __device__ __forceinline__ uint32_t a(int i, int r0) const {
-    uint32_t o = off[i];
-    opaque(o);
-    return o + (uint32_t)r0 * ars;
+    uint32_t base = (uint32_t)r0 * ars;
+    opaque_s(base);
+    return off[i] + base;
   }
-  __device__ __forceinline__ uint32_t b(int i, int r0) const {
-    uint32_t o = off[i], d = dlt;
-    opaque(o);
-    opaque(d);
-    return o + d + ((uint32_t)r0 * brs + (uint32_t)(i * (1024 / RB)) * (brs - ars));
+  __device__ __forceinline__ uint32_t b(int i, int r0) {
+    if constexpr (SAME) {
+      return a(i, r0);
+    } else {
+      uint32_t base = (uint32_t)r0 * brs + (uint32_t)(i * (1024 / RB)) * (brs - ars);
+      opaque_s(base);
+      opaque(dlt);
+      return off[i] + dlt + base;
+    }
   }
 };
 

@@ -54,7 +54,8 @@ struct FwdDCfg {
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-template <class C>
+// SAME: K and V rows are equally spaced (one loader offset serves both).
+template <class C, bool SAME>
 __global__ void __launch_bounds__(C::NT)
 __attribute__((amdgpu_waves_per_eu(C::OCC, C::OCC)))
 fwd_kernel(FwdParams P) {
@@ -98,7 +99,7 @@ fwd_kernel(FwdParams P) {
 
   // Loader: 16-byte slot `lane` of 1 KB block m of a tile comes from tile_pos(slot).
   static_assert(tile_rows_affine_ok<RB, C::LPW, C::NW>(), "loader rows");
-  const TileLoader<C::LPW, RB> tl(wave, lane, hr.krs, hr.vrs);
+  TileLoader<C::LPW, RB, SAME> tl(wave, lane, hr.krs, hr.vrs);
   auto issue = [&](int key0, char* dst) {
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i) {
@@ -369,7 +370,7 @@ fwd_kernel(FwdParams P) {
 //   LDS-DMA loads fill Kb[j%2] with K_{j+2} and Vb[(j+1)%2] with V_{j+1}, the
 //   buffers read by iteration j-1 (all waves passed the barrier ending it).
 // ---------------------------------------------------------------------------
-template <class C>
+template <class C, bool SAME>
 __global__ void __launch_bounds__(C::NT)
 __attribute__((amdgpu_waves_per_eu(C::OCC, C::OCC)))
 fwd_pipe_kernel(FwdParams P) {
@@ -401,7 +402,7 @@ fwd_pipe_kernel(FwdParams P) {
   const float tau = P.rescale_log2;
 
   static_assert(tile_rows_affine_ok<RB, C::LPW, C::NW>(), "loader rows");
-  const TileLoader<C::LPW, RB> tl(wave, lane, hr.krs, hr.vrs);
+  TileLoader<C::LPW, RB, SAME> tl(wave, lane, hr.krs, hr.vrs);
   // Key tiles t_lo + j, j = 0 .. n_tiles-1, cover the keys any row of the
   // workgroup keeps; t counts from t_lo below.
   const int t_lo = kb.lo(q0) / BN;
@@ -631,7 +632,10 @@ static hipError_t launch_fwd_pipe(const FwdParams& p0, int B, int H, hipStream_t
   p.n_qtiles = (p.N + C::BM - 1) / C::BM;
   const long long grid = (long long)p.n_qtiles * B * H;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(fwd_pipe_kernel<C>, dim3((unsigned)grid), dim3(C::NT), 0, st, p);
+  if (p.sk.r == p.sv.r)
+    hipLaunchKernelGGL((fwd_pipe_kernel<C, true>), dim3((unsigned)grid), dim3(C::NT), 0, st, p);
+  else
+    hipLaunchKernelGGL((fwd_pipe_kernel<C, false>), dim3((unsigned)grid), dim3(C::NT), 0, st, p);
   return hipGetLastError();
 }
 
@@ -641,7 +645,10 @@ static hipError_t launch_fwd_direct(const FwdParams& p0, int B, int H, hipStream
   p.n_qtiles = (p.N + C::BM - 1) / C::BM;
   const long long grid = (long long)p.n_qtiles * B * H;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(fwd_kernel<C>, dim3((unsigned)grid), dim3(C::NT), 0, st, p);
+  if (p.sk.r == p.sv.r)
+    hipLaunchKernelGGL((fwd_kernel<C, true>), dim3((unsigned)grid), dim3(C::NT), 0, st, p);
+  else
+    hipLaunchKernelGGL((fwd_kernel<C, false>), dim3((unsigned)grid), dim3(C::NT), 0, st, p);
   return hipGetLastError();
 }
 
