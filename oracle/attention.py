@@ -23,6 +23,12 @@ Conventions (the pages fix none of them; these are the plainest readings):
     rows so; a packed sequence may have no keys) has an empty sum: lse_i =
     ln 0 = -inf, and its output is taken as 0 (the sum of p_ij v_j over no
     keys), so it does not depend on Q, K or V and its gradients are 0;
+  * block sparsity (the customisation the page "FlashAttention (Metal Port)"
+    README, section "Documentation", calls easy to add to the base
+    algorithm): an optional boolean mask over (query block, key block) pairs
+    of ``block`` x ``block`` scores (128 by default) keeps score (i, j) only
+    where mask[b, h, i // block, j // block] is true, on top of causal and
+    window;
   * packed variable-length batches (``forward_varlen`` / ``backward_varlen``)
     are independent problems, one per sequence: rows cu[b] .. cu[b+1]-1 of the
     packed [total, H, D] tensors are sequence b, with these conventions inside
@@ -68,11 +74,12 @@ def key_bounds(rows, n_q, n_k, causal, window=-1):
     return lo, hi
 
 
-def scores(q, k, scale, causal, rows=None, n_q=None, window=-1):
+def scores(q, k, scale, causal, rows=None, n_q=None, window=-1, block_mask=None, block=128):
     """S[i, j] = scale * q_i . k_j for one head, masked entries set to -inf.
 
     q: [M, D] (the query rows listed in ``rows``, or all rows 0..M-1), k: [N_k, D];
-    n_q: the head's query length (default M).
+    n_q: the head's query length (default M); block_mask: this head's boolean
+    [ceil(N_q / block), ceil(N_k / block)] block mask, or None.
     """
     q = _as_f64(q)
     k = _as_f64(k)
@@ -83,6 +90,10 @@ def scores(q, k, scale, causal, rows=None, n_q=None, window=-1):
         lo, hi = key_bounds(idx, n_q, k.shape[0], causal, window)
         j = np.arange(k.shape[0])[None, :]
         s = np.where((j < lo[:, None]) | (j > hi[:, None]), -np.inf, s)
+    if block_mask is not None:
+        bm = np.asarray(block_mask, dtype=bool)
+        keep = bm[idx[:, None] // block, np.arange(k.shape[0])[None, :] // block]
+        s = np.where(keep, s, -np.inf)
     return s
 
 
@@ -101,7 +112,11 @@ def softmax_rows(s):
     return p / l1[:, None], lse
 
 
-def forward(q, k, v, causal, scale, rows=None, window=-1):
+def _head_mask(block_mask, b, h):
+    return None if block_mask is None else np.asarray(block_mask)[b, h]
+
+
+def forward(q, k, v, causal, scale, rows=None, window=-1, block_mask=None, block=128):
     """Attention forward for all heads.
 
     Args:
@@ -112,6 +127,8 @@ def forward(q, k, v, causal, scale, rows=None, window=-1):
       window: left window (keys j >= i + N_k - N_q - window), < 0 for none.
       rows: optional sorted 1-D array of query indices; when given, only those
         rows are computed (rows are independent, so this is the same result).
+      block_mask: optional boolean [B, H, ceil(N_q / block), ceil(N_k / block)]
+        mask of kept (query block, key block) pairs.
     Returns:
       O  [B, H, M, D] float64 and lse [B, H, M] float64 (M = N or len(rows)).
     """
@@ -129,14 +146,15 @@ def forward(q, k, v, causal, scale, rows=None, window=-1):
             kh = h // G
             for r0, r1 in _row_blocks(M, k.shape[2]):
                 rr = sel[r0:r1]
-                s = scores(q[b, h, rr], k[b, kh], scale, causal, rows=rr, n_q=N, window=window)
+                s = scores(q[b, h, rr], k[b, kh], scale, causal, rows=rr, n_q=N, window=window,
+                           block_mask=_head_mask(block_mask, b, h), block=block)
                 p, lse_blk = softmax_rows(s)
                 o[b, h, r0:r1] = p @ v[b, kh]
                 lse[b, h, r0:r1] = lse_blk
     return o, lse
 
 
-def backward(q, k, v, do, causal, scale, window=-1):
+def backward(q, k, v, do, causal, scale, window=-1, block_mask=None, block=128):
     """Gradients of sum(dO * O) with respect to Q, K and V, in float64.
 
     Follows the chain rule through the definition O = softmax(S) V with
@@ -162,7 +180,8 @@ def backward(q, k, v, do, causal, scale, window=-1):
     for b in range(B):
         for h in range(H):
             kh = h // G
-            s = scores(q[b, h], k[b, kh], scale, causal, window=window)
+            s = scores(q[b, h], k[b, kh], scale, causal, window=window, block_mask=_head_mask(block_mask, b, h),
+                       block=block)
             p, _ = softmax_rows(s)
             dv[b, kh] += p.T @ do[b, h]
             dp = do[b, h] @ v[b, kh].T

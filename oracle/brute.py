@@ -13,20 +13,21 @@ def _dot(a, b):
     return math.fsum(x * y for x, y in zip(a, b))
 
 
-def _keys(i, n_q, n_k, causal, window):
-    """Keys row i keeps: from i + (n_k - n_q) - window (or 0) up to i + (n_k - n_q) (or the last key)."""
+def _keys(i, n_q, n_k, causal, window, block_mask=None, block=128):
+    """Keys row i keeps: from i + (n_k - n_q) - window (or 0) up to i + (n_k - n_q) (or the last key),
+    and, with a block mask (nested lists of bools), only those whose (i // block, j // block) entry is true."""
     diag = i + n_k - n_q
     first = max(0, diag - window) if window >= 0 else 0
     last = min(n_k - 1, diag) if causal else n_k - 1
-    return list(range(first, last + 1))
+    return [j for j in range(first, last + 1) if block_mask is None or block_mask[i // block][j // block]]
 
 
-def forward(q, k, v, causal, scale, window=-1):
+def forward(q, k, v, causal, scale, window=-1, block_mask=None, block=128):
     """q: nested list [N_q][D], k, v: [N_k][D] floats for one head. Returns (O [N_q][D], lse [N_q])."""
     n = len(q)
     o, lse = [], []
     for i in range(n):
-        keys = _keys(i, n, len(k), causal, window)
+        keys = _keys(i, n, len(k), causal, window, block_mask, block)
         if not keys:  # a row that keeps no key: empty sum, lse = ln 0, output 0
             o.append([0.0] * len(v[0]) if v else [])
             lse.append(-math.inf)
@@ -40,13 +41,13 @@ def forward(q, k, v, causal, scale, window=-1):
     return o, lse
 
 
-def backward(q, k, v, do, causal, scale, window=-1):
+def backward(q, k, v, do, causal, scale, window=-1, block_mask=None, block=128):
     """Loop form of dQ, dK, dV for one head (nested lists)."""
     n, dd = len(q), len(q[0])
     nk = len(k)
     p = []
     for i in range(n):
-        kept = set(_keys(i, n, nk, causal, window))
+        kept = set(_keys(i, n, nk, causal, window, block_mask, block))
         if not kept:  # a row that keeps no key has P = 0 (its output is the constant 0)
             p.append([0.0] * nk)
             continue

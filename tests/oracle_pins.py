@@ -32,6 +32,11 @@ own code:
     all): O = 0 and lse = -inf exactly, the other rows equal torch's
     top-left causal attention of the remaining queries, with zero gradients
     for the empty rows and torch autograd for the rest;
+  * block-sparse masks: an all-true mask changes nothing; torch's
+    scaled_dot_product_attention and autograd with the element mask expanded
+    from the block mask (np.kron) and intersected with the causal / window
+    band; masking out whole key blocks equals deleting those keys; and the
+    scalar-loop brute force with a block mask;
   * packed variable-length batches: torch's scaled_dot_product_attention and
     autograd on the zero-padded batch with an explicit boolean mask built from
     the lengths (a formulation by masking, not by slicing), including empty
@@ -464,3 +469,94 @@ def pin_varlen_padded(fwd_varlen, bwd_varlen, tol=1e-11):
             keys = slice(cu_k[b], cu_k[b + 1])
             np.testing.assert_allclose(dk[keys].transpose(1, 0, 2), tk.grad.numpy()[b][:, :nk[b]], atol=tol)
             np.testing.assert_allclose(dv[keys].transpose(1, 0, 2), tv.grad.numpy()[b][:, :nk[b]], atol=tol)
+
+
+def _band(Nq, Nk, causal, w):
+    i = np.arange(Nq)[:, None]
+    j = np.arange(Nk)[None, :]
+    keep = np.ones((Nq, Nk), dtype=bool)
+    if causal:
+        keep &= j <= i + Nk - Nq
+    if w >= 0:
+        keep &= j >= i + Nk - Nq - w
+    return keep
+
+
+def pin_block_mask_all_true(fwd, bwd, tol=1e-12):
+    """A block mask that keeps every block is no mask."""
+    q, do = _rand((1, 2, 37, 8), 150), _rand((1, 2, 37, 8), 153)
+    k, v = _rand((1, 2, 45, 8), 151), _rand((1, 2, 45, 8), 152)
+    for causal, block in ((False, 4), (True, 16), (True, 128)):
+        m = np.ones((1, 2, -(-37 // block), -(-45 // block)), dtype=bool)
+        o, lse = fwd(q, k, v, causal, 0.4, block_mask=m, block=block)
+        o0, lse0 = fwd(q, k, v, causal, 0.4)
+        np.testing.assert_allclose(o, o0, atol=tol)
+        np.testing.assert_allclose(lse, lse0, atol=tol)
+        for a, b in zip(bwd(q, k, v, do, causal, 0.4, block_mask=m, block=block), bwd(q, k, v, do, causal, 0.4)):
+            np.testing.assert_allclose(a, b, atol=tol)
+
+
+def pin_block_mask_torch(fwd, bwd, tol=1e-11):
+    """torch CPU float64 sdpa + autograd with the boolean element mask kron(block_mask, ones) & band."""
+    import torch
+
+    for (B, H, Hkv, Nq, Nk, causal, w, block, seed) in [(1, 2, 2, 23, 30, False, -1, 4, 160),
+                                                         (2, 4, 2, 19, 19, True, -1, 3, 161),
+                                                         (1, 2, 1, 17, 29, True, 6, 5, 162)]:
+        q, do = _rand((B, H, Nq, D := 8), seed), _rand((B, H, Nq, D), seed + 3)
+        k, v = _rand((B, Hkv, Nk, D), seed + 1), _rand((B, Hkv, Nk, D), seed + 2)
+        nqb, nkb = -(-Nq // block), -(-Nk // block)
+        m = np.random.default_rng(seed + 4).random((B, H, nqb, nkb)) < 0.55
+        o, lse = fwd(q, k, v, causal, 0.3, window=w, block_mask=m, block=block)
+        dq, dk, dv = bwd(q, k, v, do, causal, 0.3, window=w, block_mask=m, block=block)
+        elem = np.stack([np.stack([np.kron(m[b, h], np.ones((block, block), dtype=bool))[:Nq, :Nk]
+                                   for h in range(H)]) for b in range(B)]) & _band(Nq, Nk, causal, w)
+        live = elem.any(axis=3)
+        safe = elem.copy()
+        safe[..., 0] |= ~live  # a dummy key for empty rows, whose dO is zeroed
+        tq, tk, tv = (torch.from_numpy(x).requires_grad_() for x in (q, k, v))
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(safe),
+                                                               scale=0.3, enable_gqa=True)
+        s = 0.3 * (tq @ tk.repeat_interleave(H // Hkv, dim=1).transpose(-1, -2))
+        lse_ref = torch.logsumexp(s.masked_fill(~torch.from_numpy(elem), float("-inf")), dim=-1)
+        ref.backward(torch.from_numpy(do * live[..., None]))
+        np.testing.assert_allclose(o[live], ref.detach().numpy()[live], atol=tol)
+        np.testing.assert_allclose(lse[live], lse_ref.detach().numpy()[live], atol=tol)
+        assert np.all(o[~live] == 0.0) and np.all(lse[~live] == -np.inf)
+        np.testing.assert_allclose(dq, tq.grad.numpy(), atol=tol)
+        np.testing.assert_allclose(dk, tk.grad.numpy(), atol=tol)
+        np.testing.assert_allclose(dv, tv.grad.numpy(), atol=tol)
+
+
+def pin_block_mask_drops_keys(fwd, tol=1e-12):
+    """Without causal or window, masking key blocks out of every query block equals deleting those keys."""
+    q = _rand((1, 1, 21, 8), 170)
+    k, v = _rand((1, 1, 40, 8), 171), _rand((1, 1, 40, 8), 172)
+    block = 8
+    keep_blocks = np.array([True, False, True, True, False])
+    m = np.broadcast_to(keep_blocks, (1, 1, 3, 5))
+    o, lse = fwd(q, k, v, False, 0.6, block_mask=m, block=block)
+    kept = np.repeat(keep_blocks, block)[:40]
+    o2, lse2 = fwd(q, k[:, :, kept], v[:, :, kept], False, 0.6)
+    np.testing.assert_allclose(o, o2, atol=tol)
+    np.testing.assert_allclose(lse, lse2, atol=tol)
+
+
+def pin_block_mask_brute(fwd, bwd, brute, tol=1e-12):
+    """The scalar-loop oracle with a block mask, forward and backward."""
+    for (Nq, Nk, causal, w, block, seed) in [(7, 9, False, -1, 2, 180), (8, 8, True, -1, 3, 181),
+                                             (6, 10, True, 2, 2, 182)]:
+        q, do = _rand((1, 1, Nq, 4), seed), _rand((1, 1, Nq, 4), seed + 3)
+        k, v = _rand((1, 1, Nk, 4), seed + 1), _rand((1, 1, Nk, 4), seed + 2)
+        m = np.random.default_rng(seed + 4).random((1, 1, -(-Nq // block), -(-Nk // block))) < 0.6
+        o, lse = fwd(q, k, v, causal, 0.6, window=w, block_mask=m, block=block)
+        ml = m[0, 0].tolist()
+        o_b, lse_b = brute.forward(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), causal, 0.6, window=w,
+                                   block_mask=ml, block=block)
+        np.testing.assert_allclose(o[0, 0], np.array(o_b), atol=tol)
+        np.testing.assert_allclose(lse[0, 0], np.array(lse_b), atol=tol)
+        g = bwd(q, k, v, do, causal, 0.6, window=w, block_mask=m, block=block)
+        g_b = brute.backward(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), do[0, 0].tolist(), causal, 0.6,
+                             window=w, block_mask=ml, block=block)
+        for a, b in zip(g, g_b):
+            np.testing.assert_allclose(a[0, 0], np.array(b), atol=tol)

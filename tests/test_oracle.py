@@ -98,3 +98,19 @@ def test_row_subset_matches_full():
         o_s, lse_s = attention.forward(q, k, v, causal, 0.35, rows=rows)
         np.testing.assert_allclose(o_s, o[:, :, rows], atol=1e-14)
         np.testing.assert_allclose(lse_s, lse[:, :, rows], atol=1e-14)
+
+
+def test_block_mask_all_true():
+    pins.pin_block_mask_all_true(attention.forward, attention.backward)
+
+
+def test_block_mask_torch():
+    pins.pin_block_mask_torch(attention.forward, attention.backward)
+
+
+def test_block_mask_drops_keys():
+    pins.pin_block_mask_drops_keys(attention.forward)
+
+
+def test_block_mask_brute():
+    pins.pin_block_mask_brute(attention.forward, attention.backward, brute)

@@ -333,3 +333,74 @@ def test_varlen_mutants_fail_a_pin(mutant):
 
 def test_unmutated_varlen_factory_passes():
     pins.pin_varlen_padded(*_varlen_factory())
+
+
+def _block_factory(mutant=None):
+    """The oracle with one planted mistake in the block-mask lookup: the query block taken one row
+    late, or the key block index replaced by the query's."""
+    def head_scores(qh, kh, scale, causal, window, bm, block, n_q):
+        s = attention.scores(qh, kh, scale, causal, window=window, n_q=n_q)
+        if bm is None:
+            return s
+        i = np.arange(qh.shape[0])[:, None]
+        j = np.arange(kh.shape[0])[None, :]
+        if mutant == "row_late":
+            ib = np.minimum((i + 1) // block, bm.shape[0] - 1)
+            keep = bm[ib, j // block]
+        elif mutant == "key_from_query":
+            keep = bm[i // block, np.minimum(i // block, bm.shape[1] - 1)] & np.ones_like(j, dtype=bool)
+        else:
+            keep = bm[i // block, j // block]
+        return np.where(keep, s, -np.inf)
+
+    def fwd(q, k, v, causal, scale, rows=None, window=-1, block_mask=None, block=128):
+        q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+        B, H, N, _ = q.shape
+        G = H // k.shape[1]
+        o, lse = np.empty((B, H, N, v.shape[-1])), np.empty((B, H, N))
+        for b in range(B):
+            for h in range(H):
+                bm = None if block_mask is None else np.asarray(block_mask)[b, h]
+                p, lse[b, h] = attention.softmax_rows(head_scores(q[b, h], k[b, h // G], scale, causal, window, bm,
+                                                                  block, N))
+                o[b, h] = p @ v[b, h // G]
+        return o, lse
+
+    def bwd(q, k, v, do, causal, scale, window=-1, block_mask=None, block=128):
+        q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+        dq, dk, dv = np.empty_like(q), np.zeros_like(k), np.zeros_like(v)
+        B, H, N, _ = q.shape
+        G = H // k.shape[1]
+        for b in range(B):
+            for h in range(H):
+                bm = None if block_mask is None else np.asarray(block_mask)[b, h]
+                kh, vh = k[b, h // G], v[b, h // G]
+                p, _ = attention.softmax_rows(head_scores(q[b, h], kh, scale, causal, window, bm, block, N))
+                dv[b, h // G] += p.T @ do[b, h]
+                dp = do[b, h] @ vh.T
+                ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+                dq[b, h] = scale * (ds @ kh)
+                dk[b, h // G] += scale * (ds.T @ q[b, h])
+        return dq, dk, dv
+    return fwd, bwd
+
+
+@pytest.mark.parametrize("mutant", ["row_late", "key_from_query"])
+def test_block_mask_mutants_fail_a_pin(mutant):
+    fwd, bwd = _block_factory(mutant)
+    failures = 0
+    for c in (lambda: pins.pin_block_mask_torch(fwd, bwd), lambda: pins.pin_block_mask_drops_keys(fwd),
+              lambda: pins.pin_block_mask_brute(fwd, bwd, brute)):
+        try:
+            c()
+        except (AssertionError, ValueError, IndexError):
+            failures += 1
+    assert failures >= 1
+
+
+def test_unmutated_block_factory_passes():
+    fwd, bwd = _block_factory()
+    pins.pin_block_mask_all_true(fwd, bwd)
+    pins.pin_block_mask_torch(fwd, bwd)
+    pins.pin_block_mask_drops_keys(fwd)
+    pins.pin_block_mask_brute(fwd, bwd, brute)
