@@ -172,6 +172,48 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
                   int window, float scale, int dtype, void* stream);
 
 /*
+ * Block lists of a block-sparse mask. Block sparsity keeps or drops whole
+ * 128 x 128 blocks of the score matrix: score (i, j) is kept only when the
+ * mask byte of (query block i / 128, key block j / 128) is non-zero, on top of
+ * causal and window (the block-sparsity customisation named in the
+ * "FlashAttention (Metal Port)" README, section "Documentation"). The kernels
+ * walk lists of the blocks that can hold a kept score; this call builds them
+ * once per mask, for reuse by every fa_fwd_sparse / fa_bwd_sparse call with
+ * the same mask, B, H, Nq, Nk, causal and window.
+ *   mask         : device bytes; element (b, h, qb, kb) at
+ *                  b*s0 + h*s1 + qb*s2 + kb with mask_strides = {s0, s1, s2}
+ *                  (host array, >= 0; 0 broadcasts), qb < ceil(Nq / 128),
+ *                  kb < ceil(Nk / 128), h over the H query heads.
+ *   kv_count     : device int32 [B, H, nqb] (nqb = ceil(Nq / 128)): how many
+ *                  key blocks are listed for each query block;
+ *   kv_index     : device int32 [B, H, nqb, nkb] (nkb = ceil(Nk / 128)): the
+ *                  listed key blocks, ascending, in the first kv_count entries;
+ *   q_count, q_index : the same for the query blocks of each key block
+ *                  ([B, H, nkb] and [B, H, nkb, nqb]).
+ * A block is listed when its mask byte is non-zero and it meets the causal /
+ * window band of fa_fwd_general. One small kernel on `stream`.
+ * FA_ERR_INVALID_ARG: a NULL or misaligned pointer, a negative stride,
+ * B/H/Nq/Nk < 1, causal not 0/1, window < -1.
+ */
+int fa_block_lists(const void* mask, const long long* mask_strides, int B,
+                   int H, int Nq, int Nk, int causal, int window,
+                   int* kv_count, int* kv_index, int* q_count, int* q_index,
+                   void* stream);
+
+/*
+ * Block-sparse forward: fa_fwd_general restricted to the blocks listed in
+ * kv_count / kv_index (from fa_block_lists with the same B, H, Nq, Nk, causal
+ * and window). Contiguous layouts as for fa_fwd_general; every dtype. Rows
+ * whose blocks are all dropped keep no key: O = 0, lse = -inf. Lists not made
+ * by fa_block_lists give undefined results (list reads and tile loads stay
+ * inside their buffers).
+ */
+int fa_fwd_sparse(const void* q, const void* k, const void* v, void* o,
+                  float* lse, int B, int H, int Hkv, int Nq, int Nk, int D,
+                  int causal, int window, float scale, int dtype,
+                  const int* kv_count, const int* kv_index, void* stream);
+
+/*
  * fa_fwd with an explicit conditional-rescale threshold `rescale_log2`
  * (>= 0, in base-2 units of the score): a row's reference max is moved --
  * and its accumulator rescaled -- only when a new tile's max exceeds it by
@@ -294,6 +336,20 @@ int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o,
                    int causal, int window, float scale, int dtype, int variant,
                    void* workspace, size_t workspace_bytes,
                    const long long* strides, void* stream);
+
+/*
+ * Block-sparse backward: the gradients of fa_fwd_sparse. The dQ pass walks
+ * kv_count / kv_index, the key-tile pass q_count / q_index (all four from one
+ * fa_block_lists call). Other arguments, variants and errors as for
+ * fa_bwd_general.
+ */
+int fa_bwd_sparse(const void* q, const void* k, const void* v, const void* o,
+                  const void* dO, const float* lse, void* dq, void* dk,
+                  void* dv, int B, int H, int Hkv, int Nq, int Nk, int D,
+                  int causal, int window, float scale, int dtype, int variant,
+                  const int* kv_count, const int* kv_index, const int* q_count,
+                  const int* q_index, void* workspace, size_t workspace_bytes,
+                  void* stream);
 
 /*
  * Variable-length backward: the gradients of fa_fwd_varlen.

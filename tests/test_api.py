@@ -317,3 +317,37 @@ def test_varlen_validation():
     assert b(wsb=ws - 1) == fa.FA_ERR_WORKSPACE
     assert b(variant=2) == fa.FA_ERR_INVALID_ARG
     assert b(cu_k=None) == fa.FA_ERR_INVALID_ARG
+
+
+def test_block_sparse_validation():
+    L = fa.lib()
+    st = (ctypes.c_longlong * 3)(64, 16, 4)
+    bad_st = (ctypes.c_longlong * 3)(64, -16, 4)
+
+    def lists(mask=P, strides=st, B=1, H=2, Nq=500, Nk=500, causal=1, window=-1, ptrs=(P, P, P, P)):
+        return L.fa_block_lists(mask, strides, B, H, Nq, Nk, causal, window, *ptrs, None)
+
+    assert lists(mask=None) == fa.FA_ERR_INVALID_ARG and "mask" in fa.last_error()
+    assert lists(strides=None) == fa.FA_ERR_INVALID_ARG and "mask_strides" in fa.last_error()
+    assert lists(strides=bad_st) == fa.FA_ERR_INVALID_ARG and "strides" in fa.last_error()
+    assert lists(Nq=0) == fa.FA_ERR_INVALID_ARG
+    assert lists(causal=2) == fa.FA_ERR_INVALID_ARG
+    assert lists(window=-3) == fa.FA_ERR_INVALID_ARG
+    assert lists(ptrs=(P, None, P, P)) == fa.FA_ERR_INVALID_ARG and "block-list" in fa.last_error()
+    assert lists(ptrs=(P, P, P + 2, P)) == fa.FA_ERR_INVALID_ARG and "aligned" in fa.last_error()
+
+    def fwd(kvc=P, kvi=P, D=64):
+        return L.fa_fwd_sparse(P, P, P, P, P, 1, 2, 2, 500, 500, D, 1, -1, 0.125, fa.FA_BF16, kvc, kvi, None)
+
+    assert fwd(kvc=None) == fa.FA_ERR_INVALID_ARG
+    assert fwd(kvi=P + 1) == fa.FA_ERR_INVALID_ARG
+    assert fwd(D=96) == fa.FA_ERR_UNSUPPORTED
+    ws = fa.bwd_workspace_size(1, 2, 500, 64, fa.FA_BWD_DETERMINISTIC)
+
+    def bwd(variant=fa.FA_BWD_DETERMINISTIC, qi=P, wsb=ws):
+        return L.fa_bwd_sparse(P, P, P, P, P, P, P, P, P, 1, 2, 2, 500, 500, 64, 1, -1, 0.125, fa.FA_BF16, variant,
+                               P, P, P, qi, P, wsb, None)
+
+    assert bwd(variant=2) == fa.FA_ERR_INVALID_ARG
+    assert bwd(qi=None) == fa.FA_ERR_INVALID_ARG
+    assert bwd(wsb=ws - 1) == fa.FA_ERR_WORKSPACE

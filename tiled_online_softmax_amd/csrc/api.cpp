@@ -87,7 +87,22 @@ struct Layout {
   const int* cu_q = nullptr;
   const int* cu_k = nullptr;
   int total_q = 0, total_k = 0;
+  // block lists of a block-sparse call (see fa_block_lists), else null
+  const int* kv_count = nullptr;
+  const int* kv_index = nullptr;
+  const int* q_count = nullptr;
+  const int* q_index = nullptr;
 };
+
+int blocks(int n) { return (n + fa::kBlock - 1) / fa::kBlock; }
+
+int check_lists(std::initializer_list<const int*> ps) {
+  for (const int* p : ps) {
+    if (!p) return fail(FA_ERR_INVALID_ARG, "a block-list pointer is NULL");
+    if (reinterpret_cast<uintptr_t>(p) & 3u) return fail(FA_ERR_INVALID_ARG, "block-list pointers must be 4-byte aligned");
+  }
+  return FA_OK;
+}
 
 // Contiguous [B, H, Nq, D] queries (and O, dO, dQ), [B, Hkv, Nk, D] keys and values, [B, H, Nq] lse.
 Layout contiguous(int H, int Hkv, int Nq, int Nk, int D) {
@@ -169,6 +184,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   p.sq = L.q; p.sk = L.k; p.sv = L.v; p.so = L.o;
   p.lse_b = L.lse_b; p.lse_h = L.lse_h;
   p.cu_q = L.cu_q; p.cu_k = L.cu_k; p.total_q = L.total_q; p.total_k = L.total_k;
+  p.kv_count = L.kv_count; p.kv_index = L.kv_index; p.nqb = blocks(N); p.nkb = blocks(Nk);
   p.N = N; p.Nk = Nk; p.causal = causal; p.window = window;
   p.hq = H; p.group = H / Hkv;
   p.scale_log2 = scale * fa::kLog2e;
@@ -221,6 +237,38 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
   if (!cu_seqlens_q) return fail(FA_ERR_INVALID_ARG, "cu_seqlens_q is NULL");
   return fwd_impl(q, k, v, o, lse, B, H, Hkv, max_seqlen_q, max_seqlen_k, D, causal, window, scale, dtype, 8.0f,
                   nullptr, nullptr, nullptr, packed(H, Hkv, D, cu_seqlens_q, cu_seqlens_k, total_q, total_k), stream);
+}
+
+int fa_block_lists(const void* mask, const long long* mask_strides, int B, int H, int Nq, int Nk, int causal,
+                   int window, int* kv_count, int* kv_index, int* q_count, int* q_index, void* stream) {
+  if (!mask) return fail(FA_ERR_INVALID_ARG, "mask is NULL");
+  if (!mask_strides) return fail(FA_ERR_INVALID_ARG, "mask_strides is NULL");
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return fail(FA_ERR_INVALID_ARG, "B, H, Nq, Nk must be >= 1");
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
+  if (window < -1) return fail(FA_ERR_INVALID_ARG, "window must be -1 (none) or >= 0 (got %d)", window);
+  for (int i = 0; i < 3; ++i)
+    if (mask_strides[i] < 0) return fail(FA_ERR_INVALID_ARG, "mask strides must be >= 0");
+  if (int s = check_lists({kv_count, kv_index, q_count, q_index})) return s;
+  if ((long long)B * H * blocks(Nq) * blocks(Nk) >= (1LL << 31))
+    return fail(FA_ERR_UNSUPPORTED, "block lists of %lld entries exceed 2^31", (long long)B * H * blocks(Nq) * blocks(Nk));
+  fa::BlockListParams p{};
+  p.mask = static_cast<const unsigned char*>(mask);
+  p.mb = mask_strides[0]; p.mh = mask_strides[1]; p.mq = mask_strides[2];
+  p.kv_count = kv_count; p.kv_index = kv_index; p.q_count = q_count; p.q_index = q_index;
+  p.H = H; p.Nq = Nq; p.Nk = Nk; p.causal = causal; p.window = window;
+  p.nqb = blocks(Nq); p.nkb = blocks(Nk);
+  return hip_status(fa::block_lists_launch(p, B, reinterpret_cast<hipStream_t>(stream)), "fa_block_lists launch");
+}
+
+int fa_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int Nq,
+                  int Nk, int D, int causal, int window, float scale, int dtype, const int* kv_count,
+                  const int* kv_index, void* stream) {
+  if (int s = check_lists({kv_count, kv_index})) return s;
+  Layout L = contiguous(H, Hkv, Nq, Nk, D);
+  L.kv_count = kv_count;
+  L.kv_index = kv_index;
+  return fwd_impl(q, k, v, o, lse, B, H, Hkv, Nq, Nk, D, causal, window, scale, dtype, 8.0f, nullptr, nullptr,
+                  nullptr, L, stream);
 }
 
 int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int D,
@@ -302,6 +350,8 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
   p.sq = L.q; p.sk = L.k; p.sv = L.v; p.so = L.o; p.sdo = L.dO; p.sdq = L.dq; p.sdk = L.dk; p.sdv = L.dv;
   p.lse_b = L.lse_b; p.lse_h = L.lse_h;
   p.cu_q = L.cu_q; p.cu_k = L.cu_k; p.total_q = L.total_q; p.total_k = L.total_k;
+  p.kv_count = L.kv_count; p.kv_index = L.kv_index; p.q_count = L.q_count; p.q_index = L.q_index;
+  p.nqb = blocks(N); p.nkb = blocks(Nk);
   p.ld = reinterpret_cast<float*>(workspace);
   const size_t rows = (size_t)Bp * H * Np;
   p.dq_accum = variant == FA_BWD_ATOMIC
@@ -357,6 +407,22 @@ int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o, c
   if (!strides) return fail(FA_ERR_INVALID_ARG, "strides is NULL");
   return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, B, H, Hkv, Nq, Nk, D, causal, window, scale, dtype, variant,
                   workspace, workspace_bytes, strides_from(strides, 8), stream);
+}
+
+int fa_bwd_sparse(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                  void* dq, void* dk, void* dv, int B, int H, int Hkv, int Nq, int Nk, int D, int causal, int window,
+                  float scale, int dtype, int variant, const int* kv_count, const int* kv_index, const int* q_count,
+                  const int* q_index, void* workspace, size_t workspace_bytes, void* stream) {
+  if (variant != FA_BWD_ATOMIC && variant != FA_BWD_DETERMINISTIC)
+    return fail(FA_ERR_INVALID_ARG, "variant must be FA_BWD_ATOMIC or FA_BWD_DETERMINISTIC (got %d)", variant);
+  if (int s = check_lists({kv_count, kv_index, q_count, q_index})) return s;
+  Layout L = contiguous(H, Hkv, Nq, Nk, D);
+  L.kv_count = kv_count;
+  L.kv_index = kv_index;
+  L.q_count = q_count;
+  L.q_index = q_index;
+  return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, B, H, Hkv, Nq, Nk, D, causal, window, scale, dtype, variant,
+                  workspace, workspace_bytes, L, stream);
 }
 
 int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,

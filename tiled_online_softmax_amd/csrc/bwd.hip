@@ -119,7 +119,8 @@ struct DkdvCfg {
 // PLAIN: Q and dO rows are equally spaced and every query tile's workspace
 // rows start at a multiple of 4 (fixed lengths with Nq % 4 == 0), so one loader
 // offset serves Q and dO and the per-row values arrive in 16-byte pieces.
-template <class C, bool ATOMIC, bool PLAIN>
+// SPARSE: visit only the query tiles of the blocks listed for this key block.
+template <class C, bool ATOMIC, bool PLAIN, bool SPARSE>
 __global__ void __launch_bounds__(C::NT)
 __attribute__((amdgpu_waves_per_eu(C::OCC, C::OCC)))
 bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
@@ -233,18 +234,13 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
   const int nq = kb.qhi(min(k0 + C::BK, NK) - 1) / BQ + 1;
   const float sl2 = P.scale_log2;
 
-  // Query tiles visited, head by head of the group: (hg, it) runs over
-  // [0, group) x [qt0, nq); (nhg, nit) is the tile after it.
-  int hg = 0, it = qt0;
-  auto advance = [&](int& g, int& t) {
-    if (++t == nq) {
-      t = qt0;
-      ++g;
-    }
-  };
-  // (a window can leave the first keys with no query at all: then dK = dV = 0)
-  if (qt0 < nq) {
-    issue(0, qt0 * BQ, smem);
+  // Query tiles visited, head by head of the group (dense: tiles [qt0, nq) of
+  // each head; sparse: the tiles of the listed query blocks). A window can
+  // leave the first keys with no query at all: then dK = dV = 0.
+  static_assert(!SPARSE || C::BK == kBlock, "a key tile is one mask block");
+  QueryTiles<SPARSE, BQ> qts(P, bb * P.hq + h0, kt, qt0, nq, group);
+  if (qts.valid()) {
+    issue(qts.g, qts.row(), smem);
     wait_vmem();
   }
   __syncthreads();
@@ -255,12 +251,12 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
   // them. The prefetch is waited for explicitly at the end of the tile.
   auto tile = [&](const char* __restrict__ cur, char* __restrict__ nxt, char* __restrict__ dsb,
                   const char* __restrict__ ktb) {
-    const int q0 = it * BQ;
-    const int qh = hg;  // this tile's query head within the group
-    int nhg = hg, nit = it;
-    advance(nhg, nit);
-    const bool more = nhg < group;
-    if (more) issue(nhg, nit * BQ, nxt);
+    const int q0 = qts.row();
+    const int qh = qts.g;  // this tile's query head within the group
+    QueryTiles<SPARSE, BQ> nx = qts;
+    nx.advance();
+    const bool more = nx.valid();
+    if (more) issue(nx.g, nx.row(), nxt);
     const char* qs = cur;
     const char* dos = qs + C::OFF_DO;
     const float* lds_ld = reinterpret_cast<const float*>(qs + C::OFF_LD);
@@ -413,12 +409,11 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
 
     if (more) wait_vmem();
     __syncthreads();
-    hg = nhg;
-    it = nit;
+    qts = nx;
   };
-  while (qt0 < nq && hg < group) {
+  while (qts.valid()) {
     tile(smem, smem + C::STAGE, ds_lds, kt_lds);
-    if (hg < group) tile(smem + C::STAGE, smem, ds_lds, kt_lds);
+    if (qts.valid()) tile(smem + C::STAGE, smem, ds_lds, kt_lds);
   }
 
   if (key < NK) {
@@ -458,8 +453,9 @@ struct DqCfg {
   static_assert(TILE % (1024 * NW) == 0 && BN % 32 == 0, "tile shape");
 };
 
-// SAME: K and V rows are equally spaced.
-template <class C, bool SAME>
+// SAME: K and V rows are equally spaced. SPARSE: walk only the key tiles of
+// the blocks listed for this query block.
+template <class C, bool SAME, bool SPARSE>
 __global__ void __launch_bounds__(C::NT)
 __attribute__((amdgpu_waves_per_eu(C::OCC, C::OCC)))
 bwd_dq_kernel(BwdParams P, int n_qtiles) {
@@ -509,12 +505,12 @@ bwd_dq_kernel(BwdParams P, int n_qtiles) {
 
   static_assert(tile_rows_affine_ok<RB, C::LPW, C::NW>(), "loader rows");
   TileLoader<C::LPW, RB, SAME> tl(wave, lane, krs, vrs);
-  auto issue = [&](int key0, char* kb) {
+  auto issue = [&](int first_key, char* dst) {
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i) {
       const int m = wave * C::LPW + i;
-      buf_load_lds16(rk, tl.a(i, key0), 0, (lds_void*)(kb + m * 1024));
-      buf_load_lds16(rv, tl.b(i, key0), 0, (lds_void*)(kb + C::TILE + m * 1024));
+      buf_load_lds16(rk, tl.a(i, first_key), 0, (lds_void*)(dst + m * 1024));
+      buf_load_lds16(rv, tl.b(i, first_key), 0, (lds_void*)(dst + C::TILE + m * 1024));
     }
   };
   // One base register per operand kind (see the key-tile pass).
@@ -526,19 +522,24 @@ bwd_dq_kernel(BwdParams P, int n_qtiles) {
 #pragma unroll
   for (int e = 0; e < NE; ++e) acc[e] = f32x16{};
 
-  // key tiles [t_lo, t_end) hold every key a row of this workgroup keeps
-  const int t_lo = kb.lo(q0) / BN;
-  const int t_end = kb.hi(min(q0 + C::BM, N) - 1) / BN + 1;
+  // the workgroup's key tiles j = 0 .. n_tiles-1 (dense: every tile holding a
+  // key one of its rows keeps; sparse: the tiles of the listed key blocks)
+  static_assert(!SPARSE || (C::BM == kBlock && kBlock % BN == 0), "a query tile is one mask block");
+  const KeyTiles<SPARSE, BN> ts(P, bh, kb, q0, q0 + C::BM);
+  const int n_tiles = ts.n;
 
-  issue(t_lo * BN, smem);
-  wait_vmem();
+  if (n_tiles > 0) {
+    issue(ts.at_clamped(0) * BN, smem);
+    wait_vmem();
+  }
   __syncthreads();
 
   // One key tile; see the key-tile pass for the restrict qualifiers.
-  auto tile = [&](int t, const char* __restrict__ cur, char* __restrict__ nxt) {
-    const int key0 = t * BN;
-    const bool more = t + 1 < t_end;
-    if (more) issue(key0 + BN, nxt);
+  int key0 = ts.at_clamped(0) * BN, key1 = ts.at_clamped(1) * BN;  // tiles j and j+1 (list reads run ahead)
+  auto tile = [&](int j, const char* __restrict__ cur, char* __restrict__ nxt) {
+    const int key2 = ts.at_clamped(j + 2) * BN;  // read now, used by the next tile
+    const bool more = j + 1 < n_tiles;
+    if (more) issue(key1, nxt);
     const char* ks = cur;
     const char* vs = ks + C::TILE;
     opaque(kbase);
@@ -627,10 +628,12 @@ bwd_dq_kernel(BwdParams P, int n_qtiles) {
     }
     if (more) wait_vmem();
     __syncthreads();
+    key0 = key1;
+    key1 = key2;
   };
-  for (int t = t_lo; t < t_end; t += 2) {
-    tile(t, smem, smem + C::STAGE);
-    if (t + 1 < t_end) tile(t + 1, smem + C::STAGE, smem);
+  for (int j = 0; j < n_tiles; j += 2) {
+    tile(j, smem, smem + C::STAGE);
+    if (j + 1 < n_tiles) tile(j + 1, smem + C::STAGE, smem);
   }
 
   if (qrow < N) {
@@ -676,10 +679,12 @@ static hipError_t launch_bwd(int variant, const BwdParams& p, int B, int H, hipS
     const int nk = (p.Nk + KCA::BK - 1) / KCA::BK;
     const long long gk = (long long)nk * B * HKV;
     if (gk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    if (plain)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<KCA, true, true>), dim3((unsigned)gk), dim3(KCA::NT), 0, st, p, nk);
+    if (p.q_index)  // block-sparse
+      hipLaunchKernelGGL((bwd_dkdv_kernel<KCA, true, false, true>), dim3((unsigned)gk), dim3(KCA::NT), 0, st, p, nk);
+    else if (plain)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<KCA, true, true, false>), dim3((unsigned)gk), dim3(KCA::NT), 0, st, p, nk);
     else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<KCA, true, false>), dim3((unsigned)gk), dim3(KCA::NT), 0, st, p, nk);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<KCA, true, false, false>), dim3((unsigned)gk), dim3(KCA::NT), 0, st, p, nk);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int Np = p.cu_q ? p.total_q : p.N, nb = row_blocks<KCA::D>(Np);
     hipLaunchKernelGGL(bwd_dq_convert_kernel<KCA::D>, dim3((unsigned)((long long)nb * (p.rows / Np))), dim3(256), 0,
@@ -689,19 +694,23 @@ static hipError_t launch_bwd(int variant, const BwdParams& p, int B, int H, hipS
   const int nk = (p.Nk + KCD::BK - 1) / KCD::BK;
   const long long gk = (long long)nk * B * HKV;
   if (gk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  if (plain)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<KCD, false, true>), dim3((unsigned)gk), dim3(KCD::NT), 0, st, p, nk);
+  if (p.q_index)  // block-sparse
+    hipLaunchKernelGGL((bwd_dkdv_kernel<KCD, false, false, true>), dim3((unsigned)gk), dim3(KCD::NT), 0, st, p, nk);
+  else if (plain)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<KCD, false, true, false>), dim3((unsigned)gk), dim3(KCD::NT), 0, st, p, nk);
   else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<KCD, false, false>), dim3((unsigned)gk), dim3(KCD::NT), 0, st, p, nk);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<KCD, false, false, false>), dim3((unsigned)gk), dim3(KCD::NT), 0, st, p, nk);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (variant == 2) return hipSuccess;  // dK/dV only
   const int nq = (p.N + QC::BM - 1) / QC::BM;
   const long long gq = (long long)nq * B * H;
   if (gq > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  if (p.sk.r == p.sv.r)
-    hipLaunchKernelGGL((bwd_dq_kernel<QC, true>), dim3((unsigned)gq), dim3(QC::NT), 0, st, p, nq);
+  if (p.kv_index)  // block-sparse calls take contiguous layouts
+    hipLaunchKernelGGL((bwd_dq_kernel<QC, true, true>), dim3((unsigned)gq), dim3(QC::NT), 0, st, p, nq);
+  else if (p.sk.r == p.sv.r)
+    hipLaunchKernelGGL((bwd_dq_kernel<QC, true, false>), dim3((unsigned)gq), dim3(QC::NT), 0, st, p, nq);
   else
-    hipLaunchKernelGGL((bwd_dq_kernel<QC, false>), dim3((unsigned)gq), dim3(QC::NT), 0, st, p, nq);
+    hipLaunchKernelGGL((bwd_dq_kernel<QC, false, false>), dim3((unsigned)gq), dim3(QC::NT), 0, st, p, nq);
   return hipGetLastError();
 }
 

@@ -21,6 +21,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 enum class Elt { F32, BF16, FP8 };
 
+// Rows (and columns) of a block of a block-sparse mask.
+constexpr int kBlock = 128;
+
 template <Elt E> struct EltInfo;
 template <> struct EltInfo<Elt::F32> { static constexpr int bytes = 4; };
 template <> struct EltInfo<Elt::BF16> { static constexpr int bytes = 2; };

@@ -55,7 +55,8 @@ struct FwdDCfg {
 };
 
 // SAME: K and V rows are equally spaced (one loader offset serves both).
-template <class C, bool SAME>
+// SPARSE: walk only the key tiles of the blocks listed for this query block.
+template <class C, bool SAME, bool SPARSE>
 __global__ void __launch_bounds__(C::NT)
 __attribute__((amdgpu_waves_per_eu(C::OCC, C::OCC)))
 fwd_kernel(FwdParams P) {
@@ -100,12 +101,12 @@ fwd_kernel(FwdParams P) {
   // Loader: 16-byte slot `lane` of 1 KB block m of a tile comes from tile_pos(slot).
   static_assert(tile_rows_affine_ok<RB, C::LPW, C::NW>(), "loader rows");
   TileLoader<C::LPW, RB, SAME> tl(wave, lane, hr.krs, hr.vrs);
-  auto issue = [&](int key0, char* dst) {
+  auto issue = [&](int first_key, char* dst) {
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i) {
       const int m = wave * C::LPW + i;
-      buf_load_lds16(rk, tl.a(i, key0), 0, (lds_void*)(dst + m * 1024));
-      buf_load_lds16(rv, tl.b(i, key0), 0, (lds_void*)(dst + C::TILE + m * 1024));
+      buf_load_lds16(rk, tl.a(i, first_key), 0, (lds_void*)(dst + m * 1024));
+      buf_load_lds16(rv, tl.b(i, first_key), 0, (lds_void*)(dst + C::TILE + m * 1024));
     }
   };
 
@@ -135,14 +136,18 @@ fwd_kernel(FwdParams P) {
   for (int e = 0; e < NE; ++e) acc[e] = f32x16{};
   float m_ref = -INFINITY, l_part = 0.f;
 
-  // key tiles [t_lo, t_end) hold every key a row of this workgroup keeps;
-  // this wave's rows keep none past tile w_end
-  const int t_lo = kb.lo(q0) / BN;
-  const int t_end = kb.hi(min(q0 + C::BM, N) - 1) / BN + 1;
-  const int w_end = min(t_end, kb.hi(qw + 31) / BN + 1);
+  // The workgroup's key tiles, j = 0 .. n_tiles-1: dense, the tiles
+  // [t_lo, t_end) that hold every key a row of it keeps; sparse, the tiles of
+  // the listed key blocks (ascending). This wave's rows keep no key past hi_w.
+  static_assert(!SPARSE || (C::BM == kBlock && kBlock % BN == 0), "a query tile is one mask block");
+  const KeyTiles<SPARSE, BN> ts(P, bh, kb, q0, q0 + C::BM);
+  const int n_tiles = ts.n;
+  const int hi_w = kb.hi(qw + 31);
 
-  issue(t_lo * BN, smem);
-  wait_vmem();
+  if (n_tiles > 0) {
+    issue(ts.at_clamped(0) * BN, smem);
+    wait_vmem();
+  }
   __syncthreads();
 
   // One key/value tile. `cur` (being read) and `nxt` (being filled by the
@@ -150,13 +155,14 @@ fwd_kernel(FwdParams P) {
   // the compiler see that the transposing reads of `cur` cannot depend on the
   // prefetch, so it does not wait for the prefetch before them. The prefetch is
   // waited for explicitly (vmcnt + barrier) at the end of the tile.
-  auto tile = [&](int t, const char* __restrict__ cur, char* __restrict__ nxt) {
-    const int key0 = t * BN;
-    const bool more = (t + 1) < t_end;
-    if (more) issue(key0 + BN, nxt);
+  int key0 = ts.at_clamped(0) * BN, key1 = ts.at_clamped(1) * BN;  // tiles j and j+1 (list reads run ahead)
+  auto tile = [&](int j, const char* __restrict__ cur, char* __restrict__ nxt) {
+    const int key2 = ts.at_clamped(j + 2) * BN;  // read now, used by the next tile
+    const bool more = j + 1 < n_tiles;
+    if (more) issue(key1, nxt);
     const char* ks = cur;
     const char* vs = cur + C::TILE;
-    if (t < w_end) {
+    if (key0 <= hi_w) {
       // ---- S^T = K Q^T ----
       // K operands are read KLA pieces ahead into a register ring: the reads
       // for piece p+KLA are issued before the MFMAs of piece p (scheduling
@@ -318,10 +324,12 @@ fwd_kernel(FwdParams P) {
     }
     if (more) wait_vmem();
     __syncthreads();
+    key0 = key1;
+    key1 = key2;
   };
-  for (int t = t_lo; t < t_end; t += 2) {
-    tile(t, smem, smem + C::STAGE);
-    if (t + 1 < t_end) tile(t + 1, smem + C::STAGE, smem);
+  for (int j = 0; j < n_tiles; j += 2) {
+    tile(j, smem, smem + C::STAGE);
+    if (j + 1 < n_tiles) tile(j + 1, smem + C::STAGE, smem);
   }
 
   // ---- epilogue: O = acc / l, lse = ln(sum exp(s)) ----
@@ -370,7 +378,7 @@ fwd_kernel(FwdParams P) {
 //   LDS-DMA loads fill Kb[j%2] with K_{j+2} and Vb[(j+1)%2] with V_{j+1}, the
 //   buffers read by iteration j-1 (all waves passed the barrier ending it).
 // ---------------------------------------------------------------------------
-template <class C, bool SAME>
+template <class C, bool SAME, bool SPARSE>
 __global__ void __launch_bounds__(C::NT)
 __attribute__((amdgpu_waves_per_eu(C::OCC, C::OCC)))
 fwd_pipe_kernel(FwdParams P) {
@@ -403,24 +411,25 @@ fwd_pipe_kernel(FwdParams P) {
 
   static_assert(tile_rows_affine_ok<RB, C::LPW, C::NW>(), "loader rows");
   TileLoader<C::LPW, RB, SAME> tl(wave, lane, hr.krs, hr.vrs);
-  // Key tiles t_lo + j, j = 0 .. n_tiles-1, cover the keys any row of the
-  // workgroup keeps; t counts from t_lo below.
-  const int t_lo = kb.lo(q0) / BN;
-  const int n_tiles = kb.hi(min(q0 + C::BM, N) - 1) / BN + 1 - t_lo;
-  // tiles [0, n_live) hold keys this wave's queries may keep (every wave starts at t_lo: rows
-  // whose window starts later see fully masked tiles first, which add nothing)
-  const int n_live = min(n_tiles, kb.hi(qw + 31) / BN + 1 - t_lo);
+  // The workgroup's key tiles j = 0 .. n_tiles-1 (ts.at(j): dense from t_lo,
+  // or the tiles of the listed key blocks) cover the keys any of its rows keeps.
+  static_assert(!SPARSE || (C::BM == kBlock && kBlock % BN == 0), "a query tile is one mask block");
+  const KeyTiles<SPARSE, BN> ts(P, bh, kb, q0, q0 + C::BM);
+  const int n_tiles = ts.n;
+  // tiles [0, n_live) hold keys this wave's queries may keep (every wave starts at the first tile:
+  // rows whose window starts later see fully masked tiles first, which add nothing)
+  const int n_live = ts.live_count(kb.hi(qw + 31));
 
-  // K tile t (counted from t_lo) into dst; V tile t into dst
-  auto issue_k = [&](int t, char* dst) {
+  // K (V) of the tile starting at key key0 into dst
+  auto issue_k = [&](int first_key, char* dst) {
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i)
-      buf_load_lds16(rk, tl.a(i, (t_lo + t) * BN), 0, (lds_void*)(dst + (wave * C::LPW + i) * 1024));
+      buf_load_lds16(rk, tl.a(i, first_key), 0, (lds_void*)(dst + (wave * C::LPW + i) * 1024));
   };
-  auto issue_v = [&](int t, char* dst) {
+  auto issue_v = [&](int first_key, char* dst) {
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i)
-      buf_load_lds16(rv, tl.b(i, (t_lo + t) * BN), 0, (lds_void*)(dst + (wave * C::LPW + i) * 1024));
+      buf_load_lds16(rv, tl.b(i, first_key), 0, (lds_void*)(dst + (wave * C::LPW + i) * 1024));
   };
 
   i32x4 qf[NP];
@@ -511,11 +520,10 @@ fwd_pipe_kernel(FwdParams P) {
 
   // ---- mask + row max of a score tile, then the conditional rescale ----
   // with_pv: P.V MFMAs of the previous tile run interleaved (vt = its V tile).
-  auto pv_and_max = [&](const bool with_pv, const bool with_max, const char* __restrict__ vt, int t,
+  auto pv_and_max = [&](const bool with_pv, const bool with_max, const char* __restrict__ vt, int key0,
                         f32x16 (&s)[NB], bool use_max) __attribute__((always_inline)) {
     if (with_max && use_max) {
-      // key key0 + 4h + r of tile t (r = 32b + 8(v/4) + v%4) is kept iff lo <= r <= hi
-      const int key0 = (t_lo + t) * BN;
+      // key key0 + 4h + r of the tile (r = 32b + 8(v/4) + v%4) is kept iff lo <= r <= hi
       if (kb.mask_tile<BN>(key0, qw)) {
         int hi = kb.hi(qrow) - key0 - 4 * hf, lo = kb.lo(qrow) - key0 - 4 * hf;
         opaque(hi);
@@ -578,31 +586,39 @@ fwd_pipe_kernel(FwdParams P) {
   };
 
   // ---- prologue: K_0, V_0, K_1 in; S_0 and its max ----
-  issue_k(0, kb0);
-  issue_v(0, vb0);
-  if (n_tiles > 1) issue_k(1, kb1);
+  // first keys of tiles j+1 and j+2 of the coming iteration j (list reads run one iteration ahead)
+  int key1 = ts.at_clamped(1) * BN, key2 = ts.at_clamped(2) * BN;
+  if (n_tiles > 0) {
+    const int key0 = ts.at_clamped(0) * BN;
+    issue_k(key0, kb0);
+    issue_v(key0, vb0);
+  }
+  if (n_tiles > 1) issue_k(key1, kb1);
   wait_vmem();
   __syncthreads();
   if (n_live > 0) {
     scores_and_p(true, false, kb0, sa, sb);
-    pv_and_max(false, true, vb0, 0, sa, true);
+    pv_and_max(false, true, vb0, ts.at_clamped(0) * BN, sa, true);
   }
   __syncthreads();  // every wave is done with Kb[0] before K_2 overwrites it
 
   // One iteration; sc_ holds S_j on entry, sn_ receives S_{j+1}.
   auto iter = [&](int j, const char* __restrict__ kcur, const char* __restrict__ vcur, char* __restrict__ knxt,
                   char* __restrict__ vnxt, f32x16 (&sc_)[NB], f32x16 (&sn_)[NB]) __attribute__((always_inline)) {
-    if (j + 1 < n_tiles) issue_v(j + 1, vnxt);
-    if (j + 2 < n_tiles) issue_k(j + 2, knxt);
+    const int key3 = ts.at_clamped(j + 3) * BN;  // read now, used by the next iteration
+    if (j + 1 < n_tiles) issue_v(key1, vnxt);
+    if (j + 2 < n_tiles) issue_k(key2, knxt);
     opaque(kbase);
     opaque(vbase);
     if (j < n_live) {
       // the last live tile also computes (and discards) scores for the next tile
       scores_and_p(true, true, kcur, sn_, sc_);
-      pv_and_max(true, true, vcur, j + 1, sn_, j + 1 < n_live);
+      pv_and_max(true, true, vcur, key1, sn_, j + 1 < n_live);
     }
     if (j + 1 < n_tiles) wait_vmem();
     __syncthreads();
+    key1 = key2;
+    key2 = key3;
   };
   for (int j = 0; j < n_tiles; j += 2) {
     iter(j, kb1, vb0, kb0, vb1, sa, sb);
@@ -632,10 +648,12 @@ static hipError_t launch_fwd_pipe(const FwdParams& p0, int B, int H, hipStream_t
   p.n_qtiles = (p.N + C::BM - 1) / C::BM;
   const long long grid = (long long)p.n_qtiles * B * H;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  if (p.sk.r == p.sv.r)
-    hipLaunchKernelGGL((fwd_pipe_kernel<C, true>), dim3((unsigned)grid), dim3(C::NT), 0, st, p);
+  if (p.kv_index)  // block-sparse calls take contiguous layouts
+    hipLaunchKernelGGL((fwd_pipe_kernel<C, true, true>), dim3((unsigned)grid), dim3(C::NT), 0, st, p);
+  else if (p.sk.r == p.sv.r)
+    hipLaunchKernelGGL((fwd_pipe_kernel<C, true, false>), dim3((unsigned)grid), dim3(C::NT), 0, st, p);
   else
-    hipLaunchKernelGGL((fwd_pipe_kernel<C, false>), dim3((unsigned)grid), dim3(C::NT), 0, st, p);
+    hipLaunchKernelGGL((fwd_pipe_kernel<C, false, false>), dim3((unsigned)grid), dim3(C::NT), 0, st, p);
   return hipGetLastError();
 }
 
@@ -645,10 +663,12 @@ static hipError_t launch_fwd_direct(const FwdParams& p0, int B, int H, hipStream
   p.n_qtiles = (p.N + C::BM - 1) / C::BM;
   const long long grid = (long long)p.n_qtiles * B * H;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  if (p.sk.r == p.sv.r)
-    hipLaunchKernelGGL((fwd_kernel<C, true>), dim3((unsigned)grid), dim3(C::NT), 0, st, p);
+  if (p.kv_index)
+    hipLaunchKernelGGL((fwd_kernel<C, true, true>), dim3((unsigned)grid), dim3(C::NT), 0, st, p);
+  else if (p.sk.r == p.sv.r)
+    hipLaunchKernelGGL((fwd_kernel<C, true, false>), dim3((unsigned)grid), dim3(C::NT), 0, st, p);
   else
-    hipLaunchKernelGGL((fwd_kernel<C, false>), dim3((unsigned)grid), dim3(C::NT), 0, st, p);
+    hipLaunchKernelGGL((fwd_kernel<C, false, false>), dim3((unsigned)grid), dim3(C::NT), 0, st, p);
   return hipGetLastError();
 }
 

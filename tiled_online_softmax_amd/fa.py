@@ -21,9 +21,11 @@ FA_F32, FA_BF16, FA_FP8_E4M3 = 0, 1, 2
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, 1, 2, 3, 4
 FA_BWD_ATOMIC, FA_BWD_DETERMINISTIC = 0, 1
 
-EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_general", "fa_fwd_strided", "fa_fwd_varlen", "fa_fwd_ex", "fa_fwd_fp8",
-            "fa_quantize_fp8", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_gqa", "fa_bwd_general", "fa_bwd_strided",
-            "fa_bwd_varlen", "fa_bwd_dkdv", "fa_status_string", "fa_last_error")
+EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_general", "fa_fwd_strided", "fa_fwd_varlen", "fa_block_lists",
+            "fa_fwd_sparse", "fa_fwd_ex", "fa_fwd_fp8", "fa_quantize_fp8", "fa_bwd_workspace_size", "fa_bwd",
+            "fa_bwd_gqa", "fa_bwd_general", "fa_bwd_strided", "fa_bwd_sparse", "fa_bwd_varlen", "fa_bwd_dkdv",
+            "fa_status_string", "fa_last_error")
+BLOCK = 128  # rows and columns of a block of a block-sparse mask
 
 
 class FAError(RuntimeError):
@@ -48,6 +50,8 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd_general.argtypes = [_vp] * 5 + [_i] * 8 + [_f, _i, _vp]
         L.fa_fwd_strided.argtypes = [_vp] * 5 + [_i] * 8 + [_f, _i, _vp, _vp]
         L.fa_fwd_varlen.argtypes = [_vp] * 7 + [_i] * 10 + [_f, _i, _vp]
+        L.fa_block_lists.argtypes = [_vp, _vp] + [_i] * 6 + [_vp] * 5
+        L.fa_fwd_sparse.argtypes = [_vp] * 5 + [_i] * 8 + [_f, _i, _vp, _vp, _vp]
         L.fa_fwd_ex.argtypes = [_vp] * 5 + [_i] * 5 + [_f, _i, _f, _vp]
         L.fa_fwd_fp8.argtypes = [_vp] * 5 + [_i] * 5 + [_f] + [_vp] * 3 + [_vp]
         L.fa_quantize_fp8.argtypes = [_vp, _sz, _vp, _vp, _vp]
@@ -58,14 +62,15 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd_general.argtypes = [_vp] * 9 + [_i] * 8 + [_f, _i, _i, _vp, _sz, _vp]
         L.fa_bwd_strided.argtypes = [_vp] * 9 + [_i] * 8 + [_f, _i, _i, _vp, _sz, _vp, _vp]
         L.fa_bwd_varlen.argtypes = [_vp] * 11 + [_i] * 10 + [_f, _i, _i, _vp, _sz, _vp]
+        L.fa_bwd_sparse.argtypes = [_vp] * 9 + [_i] * 8 + [_f, _i, _i] + [_vp] * 4 + [_vp, _sz, _vp]
         L.fa_bwd_dkdv.argtypes = [_vp] * 8 + [_i] * 5 + [_f, _i, _vp, _sz, _vp]
         L.fa_status_string.argtypes = [_i]
         L.fa_status_string.restype = ctypes.c_char_p
         L.fa_last_error.argtypes = []
         L.fa_last_error.restype = ctypes.c_char_p
-        for name in ("fa_fwd", "fa_fwd_gqa", "fa_fwd_general", "fa_fwd_strided", "fa_fwd_varlen", "fa_fwd_ex",
-                     "fa_fwd_fp8", "fa_quantize_fp8", "fa_bwd", "fa_bwd_gqa", "fa_bwd_general", "fa_bwd_strided",
-                     "fa_bwd_varlen", "fa_bwd_dkdv"):
+        for name in ("fa_fwd", "fa_fwd_gqa", "fa_fwd_general", "fa_fwd_strided", "fa_fwd_varlen", "fa_block_lists",
+                     "fa_fwd_sparse", "fa_fwd_ex", "fa_fwd_fp8", "fa_quantize_fp8", "fa_bwd", "fa_bwd_gqa",
+                     "fa_bwd_general", "fa_bwd_strided", "fa_bwd_sparse", "fa_bwd_varlen", "fa_bwd_dkdv"):
             getattr(L, name).restype = _i
         _lib = L
     return _lib
@@ -142,13 +147,15 @@ def _dense(*ts) -> bool:
 
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False, scale: Optional[float] = None,
         rescale_log2: Optional[float] = None, out: Optional[torch.Tensor] = None,
-        lse: Optional[torch.Tensor] = None, window: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+        lse: Optional[torch.Tensor] = None, window: Optional[int] = None,
+        block_lists: Optional["BlockLists"] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Attention forward. Returns (O, lse); O is float32 for float32 inputs, bf16 otherwise.
 
     k, v may have fewer heads (grouped-query) and a different length than q (causal is then
     aligned at the bottom right); `window` (>= 0) keeps only the keys from i + Nk - Nq - window on.
     Tensors may be any [B, H, N, D] views with D contiguous (e.g. x.view(B, N, H, D).transpose(1, 2));
-    non-contiguous ones go through fa_fwd_strided.
+    non-contiguous ones go through fa_fwd_strided. `block_lists` (from block_lists()) makes the call
+    block-sparse (fa_fwd_sparse, contiguous tensors).
     """
     dense = _dense(q, k, v, out, lse)
     _check_qkv(q, kv=(k, v), same_len=False, dense=dense)
@@ -160,6 +167,15 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
         out = torch.empty(q.shape, dtype=torch.float32 if code == FA_F32 else torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if block_lists is not None:
+        if not dense or rescale_log2 is not None:
+            raise ValueError("block-sparse calls take contiguous tensors and the default rescale threshold")
+        bl = block_lists
+        bl.check(B, H, N, Nk, causal, window)
+        _check(lib().fa_fwd_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,
+                                   Hkv, N, Nk, D, int(causal), -1 if window is None else int(window), scale, code,
+                                   bl.kv_count.data_ptr(), bl.kv_index.data_ptr(), _stream(q)))
+        return out, lse
     if not dense:
         if rescale_log2 is not None:
             raise ValueError("rescale_log2 is only taken with contiguous tensors")
@@ -231,7 +247,8 @@ def bwd_workspace_size(B: int, H: int, N: int, D: int, variant: int = FA_BWD_ATO
 
 
 def bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None, variant: int = FA_BWD_ATOMIC,
-        workspace: Optional[torch.Tensor] = None, dq=None, dk=None, dv=None, window: Optional[int] = None):
+        workspace: Optional[torch.Tensor] = None, dq=None, dk=None, dv=None, window: Optional[int] = None,
+        block_lists: Optional["BlockLists"] = None):
     """Attention backward (bf16). Returns (dQ, dK, dV) as bf16 tensors; dK, dV have k's shape.
 
     Non-contiguous [B, H, N, D] views (D contiguous) go through fa_bwd_strided."""
@@ -248,6 +265,17 @@ def bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None
     dq = torch.empty(q.shape, dtype=q.dtype, device=q.device) if dq is None else dq
     dk = torch.empty(k.shape, dtype=k.dtype, device=k.device) if dk is None else dk
     dv = torch.empty(v.shape, dtype=v.dtype, device=v.device) if dv is None else dv
+    if block_lists is not None:
+        if not dense:
+            raise ValueError("block-sparse calls take contiguous tensors")
+        bl = block_lists
+        bl.check(B, H, N, Nk, causal, window)
+        _check(lib().fa_bwd_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                   lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, Nk, D,
+                                   int(causal), -1 if window is None else int(window), scale, _dtype_code(q),
+                                   variant, bl.kv_count.data_ptr(), bl.kv_index.data_ptr(), bl.q_count.data_ptr(),
+                                   bl.q_index.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(q)))
+        return dq, dk, dv
     if not dense:
         for t, like in ((dq, q), (dk, k), (dv, v)):
             if t.shape != like.shape or t.stride(-1) != 1:
@@ -347,3 +375,36 @@ def bwd_varlen(q, k, v, o, do, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: in
                                int(causal), -1 if window is None else int(window), scale, _dtype_code(q), variant,
                                workspace.data_ptr(), workspace.numel(), _stream(q)))
     return dq, dk, dv
+
+
+class BlockLists:
+    """Device block lists of a block-sparse mask (fa_block_lists) and the geometry they were built for."""
+
+    def __init__(self, kv_count, kv_index, q_count, q_index, geometry):
+        self.kv_count, self.kv_index, self.q_count, self.q_index = kv_count, kv_index, q_count, q_index
+        self.geometry = geometry
+
+    def check(self, B, H, Nq, Nk, causal, window):
+        if self.geometry != (B, H, Nq, Nk, bool(causal), -1 if window is None else int(window)):
+            raise ValueError(f"block lists were built for {self.geometry}, not {(B, H, Nq, Nk, causal, window)}")
+
+
+def block_lists(mask: torch.Tensor, Nq: int, Nk: int, causal: bool = False, window: Optional[int] = None
+                ) -> BlockLists:
+    """Block lists of a [B, H, ceil(Nq / 128), ceil(Nk / 128)] mask (bool or uint8 device tensor, the last
+    dimension contiguous; zero strides broadcast) for fwd(..., block_lists=) and bwd(..., block_lists=)."""
+    if mask.dim() != 4 or not mask.is_cuda or mask.dtype not in (torch.bool, torch.uint8) or mask.stride(3) != 1:
+        raise ValueError("mask must be a [B, H, nqb, nkb] bool/uint8 device tensor with the last dimension contiguous")
+    B, H, nqb, nkb = mask.shape
+    if nqb != -(-Nq // BLOCK) or nkb != -(-Nk // BLOCK):
+        raise ValueError(f"mask must have ceil(Nq/{BLOCK}) x ceil(Nk/{BLOCK}) blocks")
+    dev = mask.device
+    kv_count = torch.empty((B, H, nqb), dtype=torch.int32, device=dev)
+    kv_index = torch.empty((B, H, nqb, nkb), dtype=torch.int32, device=dev)
+    q_count = torch.empty((B, H, nkb), dtype=torch.int32, device=dev)
+    q_index = torch.empty((B, H, nkb, nqb), dtype=torch.int32, device=dev)
+    st = (ctypes.c_longlong * 3)(*[mask.stride(i) for i in range(3)])
+    w = -1 if window is None else int(window)
+    _check(lib().fa_block_lists(mask.data_ptr(), st, B, H, Nq, Nk, int(causal), w, kv_count.data_ptr(),
+                                kv_index.data_ptr(), q_count.data_ptr(), q_index.data_ptr(), _stream(mask)))
+    return BlockLists(kv_count, kv_index, q_count, q_index, (B, H, Nq, Nk, bool(causal), w))
