@@ -144,19 +144,48 @@ def breakdown():
         t0 = time.time()
         x = device_inputs(w, with_grad=(w.passes != "fwd"))
         legs = []  # (label, pass, fn, flops, peak, iters)
-        if w.dtype == "fp8":
+        if w.lengths is not None:  # packed sequences
+            cu = torch.from_numpy(w.cu_seqlens()).to("cuda:0")
+            mx = max(w.lengths)
+            o, lse = fa.fwd_varlen(x["q"], x["k"], x["v"], cu, cu, mx, mx, causal=w.causal)
+            ws = torch.empty(fa.bwd_workspace_size(1, w.H, w.shape[0], w.D, fa.FA_BWD_DETERMINISTIC),
+                             dtype=torch.uint8, device="cuda:0")
+            g = [torch.empty_like(x[n]) for n in ("q", "k", "v")]
+            legs.append((name + ":fwd", "fwd", lambda: fa.fwd_varlen(x["q"], x["k"], x["v"], cu, cu, mx, mx,
+                                                                   causal=w.causal, out=o, lse=lse),
+                         w.fwd_flops(), PEAK_TFLOPS["bf16"], 50))
+            legs.append((name + ":bwd", "bwd", lambda: fa.bwd_varlen(x["q"], x["k"], x["v"], o, x["do"], lse, cu, cu,
+                                                                   mx, mx, causal=w.causal,
+                                                                   variant=fa.FA_BWD_DETERMINISTIC, workspace=ws,
+                                                                   dq=g[0], dk=g[1], dv=g[2]),
+                         w.bwd_flops(), PEAK_TFLOPS["bf16"], 20))
+        elif w.block_pattern is not None:  # block-sparse; the lists are built once, outside the timed calls
+            mask = torch.from_numpy(w.block_mask()).to("cuda:0").expand(w.B, w.H, -1, -1)
+            bl = fa.block_lists(mask, w.N, w.N, w.causal, w.window)
+            o, lse = fa.fwd(x["q"], x["k"], x["v"], causal=w.causal, window=w.window, block_lists=bl)
+            ws = torch.empty(fa.bwd_workspace_size(w.B, w.H, w.N, w.D, fa.FA_BWD_DETERMINISTIC), dtype=torch.uint8,
+                             device="cuda:0")
+            legs.append((name + ":fwd", "fwd", lambda: fa.fwd(x["q"], x["k"], x["v"], causal=w.causal,
+                                                            window=w.window, block_lists=bl, out=o, lse=lse),
+                         w.fwd_flops(), PEAK_TFLOPS["bf16"], 50))
+            legs.append((name + ":bwd", "bwd", lambda: fa.bwd(x["q"], x["k"], x["v"], o, x["do"], lse,
+                                                            causal=w.causal, window=w.window,
+                                                            variant=fa.FA_BWD_DETERMINISTIC, workspace=ws,
+                                                            block_lists=bl),
+                         w.bwd_flops(), PEAK_TFLOPS["bf16"], 20))
+        elif w.dtype == "fp8":
             qc, qd = fa.quantize_fp8(x["q"])
             kc, kd = fa.quantize_fp8(x["k"])
             vc, vd = fa.quantize_fp8(x["v"])
             del x
             fn = lambda: fa.fwd_fp8(qc, kc, vc, causal=w.causal, q_descale=qd, k_descale=kd, v_descale=vd)
             legs.append((name, "fwd", fn, w.fwd_flops(), PEAK_TFLOPS["fp8"], 10))
-        if w.passes in ("fwd", "fwd+bwd") and w.dtype != "fp8":
+        if w.passes in ("fwd", "fwd+bwd") and w.dtype != "fp8" and w.lengths is None and w.block_pattern is None:
             fn = lambda: fa.fwd(x["q"], x["k"], x["v"], causal=w.causal, window=w.window)
             peak = PEAK_TFLOPS["f32" if w.dtype == "f32" else "bf16"]
             legs.append((name if w.passes == "fwd" else name + ":fwd", "fwd", fn, w.fwd_flops(), peak,
                          200 if w.N <= 2048 else 30))
-        if w.passes in ("bwd", "fwd+bwd"):
+        if w.passes in ("bwd", "fwd+bwd") and w.lengths is None and w.block_pattern is None:
             o, lse = fa.fwd(x["q"], x["k"], x["v"], causal=w.causal, window=w.window)
             ws = torch.empty(fa.bwd_workspace_size(w.B, w.H, w.N, w.D, fa.FA_BWD_DETERMINISTIC), dtype=torch.uint8,
                              device="cuda:0")

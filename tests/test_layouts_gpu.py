@@ -206,3 +206,36 @@ def test_rows_without_keys(D):
     torch.cuda.synchronize()
     o_ref, lse_ref = attention.forward(ref32["q"], ref32["k"], ref32["v"], True, 0.125)
     assert np.all(to_f64(lse32)[:, :, :160] == -np.inf) and max_abs(to_f64(o32), o_ref) <= TOL_F32
+
+
+def test_workload_varlen_bf16():
+    """The packed 16-sequence workload at full size, as the bench launches it: forward rows of five sequences
+    (the four shortest in full, sampled rows of the longest) and the backward of the shortest three."""
+    from tiled_online_softmax_amd import inputs
+    from gpu_util import sample_rows
+    w = inputs.WORKLOADS["varlen_bf16"]
+    dev, ref = prepare("bf16", w.shape, w.seed, with_grad=True, kv_shape=w.kv_shape)
+    cu = w.cu_seqlens()
+    tcu = torch.from_numpy(cu).to(DEV)
+    mx = max(w.lengths)
+    o, lse = fa.fwd_varlen(dev["q"], dev["k"], dev["v"], tcu, tcu, mx, mx, causal=True)
+    g = fa.bwd_varlen(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, tcu, tcu, mx, mx, causal=True,
+                      variant=fa.FA_BWD_DETERMINISTIC)
+    torch.cuda.synchronize()
+    og, lg = to_f64(o), to_f64(lse)
+    for b in (0, 12, 13, 14, 15):
+        s = slice(cu[b], cu[b + 1])
+        n = cu[b + 1] - cu[b]
+        rows = sample_rows(n) if n > 1024 else np.arange(n)
+        t = lambda x: x[s].transpose(1, 0, 2)[None]
+        o_ref, lse_ref = attention.forward(t(ref["q"]), t(ref["k"]), t(ref["v"]), True, w.scale, rows=rows)
+        eo = max_abs(og[s][rows].transpose(1, 0, 2)[None], o_ref)
+        el = max_abs(lg[:, s][:, rows][None], lse_ref)
+        print(f"[varlen workload seq {b} n={n}] O {eo:.3e} lse {el:.3e}", flush=True)
+        assert eo <= TOL_BF16_O and el <= TOL_BF16_LSE
+    for b in (13, 14, 15):
+        s = slice(cu[b], cu[b + 1])
+        t = lambda x: x[s].transpose(1, 0, 2)[None]
+        g_ref = attention.backward(t(ref["q"]), t(ref["k"]), t(ref["v"]), t(ref["do"]), True, w.scale)
+        for a, r in zip(g, g_ref):
+            assert max_abs(to_f64(a)[s].transpose(1, 0, 2)[None], r) <= TOL_BF16_GRAD

@@ -175,3 +175,32 @@ def test_sparse_fp8_forward_runs_the_listed_blocks():
     o_ref, lse_ref = attention.forward(vals[0], vals[1], vals[2], True, 1 / math.sqrt(D), block_mask=m)
     live = lse_ref != -np.inf
     assert max_abs(to_f64(o), o_ref) <= 6e-2 and max_abs(to_f64(lse)[live], lse_ref[live]) <= 6e-2
+
+
+def test_workload_sparse_bf16():
+    """The block-sparse workload (B2 H16 N8192 D128 causal, banded + global + strided blocks) at full size,
+    as the bench launches it: sampled forward rows of two heads and every gradient element of one head."""
+    from tiled_online_softmax_amd import inputs
+    from gpu_util import sample_rows
+    w = inputs.WORKLOADS["sparse_bf16"]
+    dev, ref = prepare("bf16", w.shape, w.seed, with_grad=True)
+    m = w.block_mask()
+    bl = fa.block_lists(torch.from_numpy(m).to(DEV).expand(w.B, w.H, -1, -1), w.N, w.N, True)
+    o, lse = fa.fwd(dev["q"], dev["k"], dev["v"], causal=True, block_lists=bl)
+    g = fa.bwd(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, causal=True, variant=fa.FA_BWD_DETERMINISTIC,
+               block_lists=bl)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.N)
+    for b, h in ((0, 0), (1, 15)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        o_ref, lse_ref = attention.forward(ref["q"][sl], ref["k"][sl], ref["v"][sl], True, w.scale, rows=rows,
+                                           block_mask=m)
+        eo = max_abs(to_f64(o)[sl][:, :, rows], o_ref)
+        el = max_abs(to_f64(lse)[sl][:, :, rows], lse_ref)
+        print(f"[sparse workload fwd b{b} h{h}] O {eo:.3e} lse {el:.3e}", flush=True)
+        assert eo <= TOL_BF16_O and el <= TOL_BF16_LSE
+    sl = (slice(1, 2), slice(7, 8))
+    g_ref = attention.backward(ref["q"][sl], ref["k"][sl], ref["v"][sl], ref["do"][sl], True, w.scale, block_mask=m)
+    errs = [max_abs(to_f64(a)[sl], r) for a, r in zip(g, g_ref)]
+    print(f"[sparse workload bwd] dQ {errs[0]:.3e} dK {errs[1]:.3e} dV {errs[2]:.3e}", flush=True)
+    assert max(errs) <= TOL_BF16_GRAD

@@ -358,8 +358,9 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqle
 
 def bwd_varlen(q, k, v, o, do, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
                causal: bool = False, scale: Optional[float] = None, window: Optional[int] = None,
-               variant: int = FA_BWD_ATOMIC, workspace=None):
-    """Gradients of fwd_varlen (bf16). Returns (dQ, dK, dV) in the packed layouts."""
+               variant: int = FA_BWD_ATOMIC, workspace=None, dq=None, dk=None, dv=None):
+    """Gradients of fwd_varlen (bf16). Returns (dQ, dK, dV) in the packed layouts (new dK, dV are zeroed
+    first: key rows outside every sequence are not written)."""
     _check_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k)
     Tq, H, D = q.shape
     Tk, Hkv = k.shape[0], k.shape[1]
@@ -368,7 +369,9 @@ def bwd_varlen(q, k, v, o, do, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: in
     need = bwd_workspace_size(1, H, Tq, D, variant)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    dq, dk, dv = torch.empty_like(q), torch.zeros_like(k), torch.zeros_like(v)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.zeros_like(k) if dk is None else dk
+    dv = torch.zeros_like(v) if dv is None else dv
     _check(lib().fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
                                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cu_seqlens_q.data_ptr(),
                                cu_seqlens_k.data_ptr(), B, H, Hkv, Tq, Tk, int(max_seqlen_q), int(max_seqlen_k), D,

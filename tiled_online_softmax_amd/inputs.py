@@ -16,7 +16,7 @@ Recipe (the same everywhere):
 from __future__ import annotations
 
 import dataclasses
-from typing import Dict, Optional
+from typing import Dict, Optional, Tuple
 
 import numpy as np
 
@@ -40,6 +40,10 @@ class Workload:
     hkv: Optional[int] = None  # K/V heads (grouped-query attention); None means H
     nk: Optional[int] = None   # key length; None means N (causal is aligned at the bottom right)
     window: Optional[int] = None  # left window; None means none
+    # Packed sequences: their lengths (queries = keys within a sequence); B = len(lengths), N = max.
+    lengths: Optional[Tuple[int, ...]] = None
+    # Block sparsity: the name of a block-mask pattern (see block_mask).
+    block_pattern: Optional[str] = None
 
     @property
     def scale(self) -> float:
@@ -47,16 +51,52 @@ class Workload:
 
     @property
     def shape(self):
+        """[B, H, N, D], or [total rows, H, D] for packed sequences."""
+        if self.lengths is not None:
+            return (int(sum(self.lengths)), self.H, self.D)
         return (self.B, self.H, self.N, self.D)
 
     @property
     def kv_shape(self):
-        return (self.B, self.H if self.hkv is None else self.hkv, self.N if self.nk is None else self.nk, self.D)
+        hkv = self.H if self.hkv is None else self.hkv
+        if self.lengths is not None:
+            return (int(sum(self.lengths)), hkv, self.D)
+        return (self.B, hkv, self.N if self.nk is None else self.nk, self.D)
+
+    def cu_seqlens(self) -> np.ndarray:
+        """int32 [B + 1] row offsets of the packed sequences."""
+        return np.concatenate([[0], np.cumsum(self.lengths)]).astype(np.int32)
+
+    def block_mask(self) -> np.ndarray:
+        """Boolean [1, 1, nqb, nkb] block mask (128 x 128 blocks, the same for every head) of the pattern:
+        "local_global_strided" keeps a query block's own and previous key blocks, key block 0 and every
+        4th key block (a banded pattern with global and strided blocks)."""
+        nqb, nkb = -(-self.N // 128), -(-(self.N if self.nk is None else self.nk) // 128)
+        qb = np.arange(nqb)[:, None]
+        kb = np.arange(nkb)[None, :]
+        if self.block_pattern == "local_global_strided":
+            m = (kb >= qb - 1) & (kb <= qb) | (kb == 0) | (kb % 4 == 0)
+        else:
+            raise ValueError(f"unknown block pattern {self.block_pattern!r}")
+        return m[None, None]
 
     def pairs(self) -> float:
-        """(query, key) pairs one head computes: N^2, halved for causal with equal lengths and no window;
-        otherwise the exact count of kept pairs."""
+        """(query, key) pairs one head of one batch entry computes (the mean over entries for packed
+        sequences): N^2, halved for causal with equal lengths, no window and no block mask; otherwise the
+        exact count of kept pairs."""
+        if self.lengths is not None:
+            n = np.asarray(self.lengths, dtype=np.float64)
+            return float((n * (n + 1) / 2 if self.causal else n * n).sum() / len(n))
         nk = self.N if self.nk is None else self.nk
+        if self.block_pattern is not None:
+            i = np.arange(self.N, dtype=np.int64)[:, None]
+            j = np.arange(nk, dtype=np.int64)[None, :]
+            keep = self.block_mask()[0, 0][i // 128, j // 128]
+            if self.causal:
+                keep &= j <= i + nk - self.N
+            if self.window is not None:
+                keep &= j >= i + nk - self.N - self.window
+            return float(keep.sum())
         if self.window is None and (not self.causal or nk == self.N):
             return self.N * nk / 2.0 if self.causal else float(self.N * nk)
         i = np.arange(self.N, dtype=np.int64)
@@ -88,6 +128,13 @@ WORKLOADS: Dict[str, Workload] = {
     "prefill_bf16": Workload("prefill_bf16", 4, 16, 1024, 128, "bf16", True, "fwd+bwd", seed=SEED_BASE + 7, nk=4096),
     # Sliding window: every row keeps the 1024 keys ending at its diagonal.
     "swa_bf16": Workload("swa_bf16", 2, 16, 8192, 128, "bf16", True, "fwd+bwd", seed=SEED_BASE + 8, window=1023),
+    # Packed batch of 16 causal sequences of mixed lengths (18,329 rows).
+    "varlen_bf16": Workload("varlen_bf16", 16, 16, 4096, 128, "bf16", True, "fwd+bwd", seed=SEED_BASE + 9,
+                            lengths=(4096, 3000, 2048, 2048, 1500, 1024, 1024, 1000, 800, 512, 512, 300, 256, 128,
+                                     64, 17)),
+    # Block-sparse causal attention: banded + global + strided 128 x 128 blocks.
+    "sparse_bf16": Workload("sparse_bf16", 2, 16, 8192, 128, "bf16", True, "fwd+bwd", seed=SEED_BASE + 10,
+                            block_pattern="local_global_strided"),
 }
 
 
