@@ -54,6 +54,7 @@ def parse():
 
 KERNEL_SOURCES = ("tiled_online_softmax_amd/csrc/bwd.hip", "tiled_online_softmax_amd/csrc/common.hpp")
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_bwd_dkdv.json")
+MFMA_RECORD = os.path.join(ROOT, "profiles", "mfma_util_step.json")
 
 
 def sources_sha256():
@@ -67,6 +68,40 @@ def sources_sha256():
             text = re.sub(r"//[^\n]*", "", fh.read())
         h.update("\n".join(l.rstrip() for l in text.splitlines() if l.strip()).encode())
     return h.hexdigest()
+
+
+def _hash_files(paths):
+    import hashlib
+    import re
+
+    h = hashlib.sha256()
+    for f in paths:
+        with open(os.path.join(ROOT, f)) as fh:
+            text = re.sub(r"//[^\n]*", "", fh.read())
+        h.update("\n".join(l.rstrip() for l in text.splitlines() if l.strip()).encode())
+    return h.hexdigest()
+
+
+def step_sources_sha256():
+    """Hash of every kernel source (comments and blank lines removed): the step's kernels' code."""
+    d = os.path.join(ROOT, "tiled_online_softmax_amd", "csrc")
+    return _hash_files(sorted(os.path.join("tiled_online_softmax_amd", "csrc", f) for f in os.listdir(d)))
+
+
+def recorded_mfma():
+    """Per-kernel MFMA utilisation (%) and HBM GB/s of the step from the committed counter record, or None if stale."""
+    try:
+        with open(MFMA_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != step_sources_sha256():
+        return None
+    out = {}
+    for k, v in rec["kernels"].items():
+        key = next((n for n in ("fwd_pipe_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel", "bwd_pre_kernel") if n in k), k)
+        out[key] = {"mfma_util_pct": round(v["mfma_util_pct"], 1), "hbm_gbps": round(v["hbm_gbps"] or 0.0, 1)}
+    return {"kernels": out, "source": "profiles/mfma_util_mh_causal_b4h16n2048d128.md"}
 
 
 def recorded_traffic():
@@ -314,7 +349,8 @@ def main():
            "pct_of_bf16_peak": round(100 * value / PEAK_TFLOPS["bf16"], 2),
            "fwd": {"ms": round(ms_f, 5), "tflops": round(fwd_tf, 2)},
            "bwd": {"ms": round(ms_b, 5), "tflops": round(bwd_tf, 2)},
-           "roofline": roofline}
+           "roofline": roofline,
+           "rocprof": recorded_mfma()}
     del x
     torch.cuda.empty_cache()
     if not args.no_breakdown:
