@@ -137,3 +137,54 @@ def test_forward_is_deterministic():
     for _ in range(9):
         o, l = fa.fwd(dev["q"], dev["k"], dev["v"], causal=True)
         assert torch.equal(o, o0) and torch.equal(l, l0)
+
+
+# The bf16 D=128 forward has two kernels. The phase-alternating one (eight waves, 256-row query
+# tiles) takes one query head per K/V head without a window, packed sequences or block lists; the
+# 128-row-tile one takes everything else. Both do the same arithmetic in the same order per row.
+PP_N = [1, 31, 64, 255, 256, 257, 511, 600, 1025]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_d128_kernels_agree_bitwise(causal):
+    """Plain call (phase-alternating kernel) and all-true block list (128-row-tile kernel, which walks
+    the same key tiles plus fully masked ones) give identical O and lse over ragged lengths."""
+    for i, N in enumerate(PP_N):
+        dev, _ = prepare("bf16", (1, 3, N, 128), 7900 + i)
+        nb = -(-N // fa.BLOCK)
+        bl = fa.block_lists(torch.ones((1, 3, nb, nb), dtype=torch.bool, device=dev["q"].device), N, N, causal)
+        o_s, l_s = fa.fwd(dev["q"], dev["k"], dev["v"], causal=causal, block_lists=bl)
+        o_d, l_d = fa.fwd(dev["q"], dev["k"], dev["v"], causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(o_d, o_s) and torch.equal(l_d, l_s), (N, causal)
+
+
+@pytest.mark.parametrize("nq,nk", [(300, 1000), (1000, 300), (257, 1)])
+def test_bf16_d128_unequal_lengths_oracle(nq, nk):
+    """N_q != N_k (bottom-right causal and full) on the phase-alternating kernel against the oracle."""
+    for causal in (False, True):
+        dev, ref = prepare("bf16", (2, 2, nq, 128), 7950 + nq + nk, nk=nk)
+        o, lse = fa.fwd(dev["q"], dev["k"], dev["v"], causal=causal)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = attention.forward(ref["q"], ref["k"], ref["v"], causal, 1.0 / math.sqrt(128))
+        o_gpu, lse_gpu = to_f64(o), to_f64(lse)
+        if causal and nk < nq:
+            # rows before the shifted diagonal keep no key: O = 0, lse = -inf in both
+            keep = np.isfinite(lse_ref)
+            assert np.array_equal(keep, np.isfinite(lse_gpu))
+            lse_gpu, lse_ref = np.where(keep, lse_gpu, 0.0), np.where(keep, lse_ref, 0.0)
+        _check("bf16", o_gpu, lse_gpu, o_ref, lse_ref, f"Nq{nq} Nk{nk} causal={causal}")
+
+
+def test_bf16_d128_k_v_row_spacings_differ():
+    """K rows 512 bytes apart, V rows 256 apart (the kernel's two-offset loader) equal the contiguous call."""
+    dev, _ = prepare("bf16", (2, 3, 700, 128), 7990)
+    wide = torch.zeros((2, 3, 700, 256), dtype=torch.bfloat16, device=dev["q"].device)
+    wide[..., :128] = dev["k"]
+    k_view = wide[..., :128]
+    assert k_view.stride(2) == 256 and not k_view.is_contiguous()
+    for causal in (False, True):
+        o_v, l_v = fa.fwd(dev["q"], k_view, dev["v"], causal=causal)
+        o_c, l_c = fa.fwd(dev["q"], dev["k"], dev["v"], causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(o_v, o_c) and torch.equal(l_v, l_c), causal

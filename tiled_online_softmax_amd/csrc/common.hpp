@@ -337,6 +337,17 @@ struct KeyBounds {
 // vmcnt(0): all of this wave's vector-memory operations (incl. LDS DMA) done.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Workgroup execution barrier without a memory fence. It waits for no
+// outstanding memory operation (a fenced barrier waits for every LDS-DMA
+// copy still in flight) and only keeps the compiler from moving memory
+// accesses across it; for phase changes that read nothing written since the
+// last fenced barrier.
+__device__ __forceinline__ void exec_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ float dot2_bf16_sum(int packed_pair, float acc) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};

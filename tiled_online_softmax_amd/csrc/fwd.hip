@@ -642,6 +642,287 @@ fwd_pipe_kernel(FwdParams P) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 forward with two wave groups in alternating phases.
+//
+// Eight waves per workgroup, two per SIMD (waves w and w + 4). Tile step j
+// has an MFMA phase M(j) -- the scores S_j = K_j Q^T and the product
+// O^T += V_{j-1}^T P_{j-1}^T -- and a softmax phase X(j) -- mask, row max,
+// conditional rescale, exponentials, bf16 packing and row sums of S_j. Waves
+// 0-3 run M(j) while waves 4-7 run X(j-1), then the groups swap, with an
+// execution barrier between the phases: each SIMD's matrix core is fed by one
+// wave while its partner's softmax runs on the VALU. This is the overlap that
+// FA4 gets from separate softmax warps (page "FlashAttention" entity trail,
+// FlashAttention-4), arranged for two waves per CDNA4 SIMD. The two waves of
+// a SIMD own adjacent 32-row blocks, so under causal masking they see about
+// the same number of live tiles.
+//
+// K and V land in two-stage rings. Step j issues K_{j+1} and V_j, which step
+// j+1 reads, and every wave waits for its own copies before the step's
+// closing barrier. Each wave runs 1 + 2 (n_tiles + 1) barriers, a count fixed
+// by the workgroup's tile range alone.
+// ---------------------------------------------------------------------------
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+
+template <int D_, int BN_>
+struct FwdPPCfg {
+  static constexpr int D = D_, BN = BN_, NW = 8;
+  static constexpr int BM = 32 * NW;
+  static constexpr int NT = 64 * NW;
+  static constexpr int RB = D * 2;               // bytes per K / V row
+  static constexpr int TILE = BN * RB;           // one K (or V) tile
+  static constexpr int LDS = 4 * TILE;           // K and V, two stages each
+  static constexpr int LPW = TILE / 1024 / NW;   // 1 KB DMA loads per wave per tile
+  static constexpr int NP = RB / 32;             // 16-byte Q pieces per lane
+  static constexpr int NB = BN / 32, NE = D / 32, NC = BN / 16;
+  static_assert(TILE % (1024 * NW) == 0, "tile must split into whole 1 KB loads per wave");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+template <class C, bool SAME>
+__global__ void __launch_bounds__(C::NT)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+fwd_pp_kernel(FwdParams P) {
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+  constexpr int D = C::D, BN = C::BN, NB = C::NB, NE = C::NE, RB = C::RB, NP = C::NP, TILE = C::TILE, NC = C::NC;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 31, hf = lane >> 5;
+  const bool second = wave >= 4;  // the second group runs half a step behind the first
+
+  int bh, qt;
+  wg_map(P.n_qtiles, P.causal, P.group, bh, qt);
+  const HeadRows hr = head_rows<2>(P, bh);
+  const int N = hr.nq;
+  const int n_qt = (N + C::BM - 1) / C::BM;
+  if (P.causal) qt = n_qt - 1 - qt;
+  if (qt < 0 || qt >= n_qt) return;  // whole workgroup, before any barrier
+  const int q0 = qt * C::BM;
+  const int qw = q0 + 32 * (2 * (wave & 3) + (wave >> 2));
+  const int qrow = qw + li;
+
+  const KeyBounds kb{N, hr.nk, P.causal, P.window};
+  const auto rq = make_rsrc(hr.q, head_span(N, hr.qrs, RB));
+  const auto rk = make_rsrc(hr.k, head_span(hr.nk, hr.krs, RB));
+  const auto rv = make_rsrc(hr.v, head_span(hr.nk, hr.vrs, RB));
+  const float sc = P.scale_log2;
+  const float tau = P.rescale_log2;
+
+  static_assert(tile_rows_affine_ok<RB, C::LPW, C::NW>(), "loader rows");
+  TileLoader<C::LPW, RB, SAME> tl(wave, lane, hr.krs, hr.vrs);
+  const KeyTiles<false, BN> ts(P, bh, kb, q0, q0 + C::BM);
+  const int n_tiles = max(ts.n, 0);  // workgroup-uniform: it alone sets the barrier count
+  const int n_live = ts.live_count(kb.hi(qw + 31));  // tiles holding keys this wave's rows may keep
+
+  auto issue_k = [&](int first_key, char* dst) {
+#pragma unroll
+    for (int i = 0; i < C::LPW; ++i)
+      buf_load_lds16(rk, tl.a(i, first_key), 0, (lds_void*)(dst + (wave * C::LPW + i) * 1024));
+  };
+  auto issue_v = [&](int first_key, char* dst) {
+#pragma unroll
+    for (int i = 0; i < C::LPW; ++i)
+      buf_load_lds16(rv, tl.b(i, first_key), 0, (lds_void*)(dst + (wave * C::LPW + i) * 1024));
+  };
+
+  i32x4 qf[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) qf[p] = buf_load16(rq, (uint32_t)qrow * hr.qrs + 32 * p + 16 * hf);
+
+  static_assert(piece_xor_ok<RB, NP>() && tr16_xor_ok<RB, true, NE>(), "offset XOR form");
+  uint32_t kbase = tile_off<RB>(li, hf);
+  uint32_t vbase = tr16_off<RB, true>(lane, 0, 0);
+
+  f32x16 acc[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) acc[e] = f32x16{};
+  float m_ref = -INFINITY, l_part = 0.f;
+  f32x16 s[NB];   // S_j, from M(j) to X(j)
+  bf16x8 pb[NC];  // P_j, from X(j) to M(j+1)
+
+  char* const ks0 = smem;
+  char* const ks1 = smem + TILE;
+  char* const vs0 = smem + 2 * TILE;
+  char* const vs1 = smem + 3 * TILE;
+
+  // ---- M(j): S_j = K_j Q^T (if tile j is live) and O^T += V_{j-1}^T P_{j-1}^T ----
+  auto mma_phase = [&](int j, const char* __restrict__ kt, const char* __restrict__ vt) __attribute__((always_inline)) {
+    if (j >= 1 && j - 1 < n_live) {
+      s16x4 va[2][NE][2];
+#pragma unroll
+      for (int e = 0; e < NE; ++e)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) va[0][e][u] = lds_read_tr16(vt + (vbase ^ tr16_xor<RB, true>(e, u)));
+#pragma unroll
+      for (int kc = 0; kc < NC; ++kc) {
+        if (kc + 1 < NC) {
+#pragma unroll
+          for (int e = 0; e < NE; ++e)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+              va[(kc + 1) & 1][e][u] = lds_read_tr16(vt + (vbase ^ tr16_xor<RB, true>(e, u)) + (kc + 1) * 16 * RB);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int e = 0; e < NE; ++e) acc[e] = mfma_bf16(__builtin_bit_cast(bf16x8, va[kc & 1][e]), pb[kc], acc[e]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (j < n_live) {
+      constexpr int KLA = 2;
+      i32x4 ka[KLA + 1][NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) s[b] = f32x16{};
+#pragma unroll
+      for (int p = 0; p < KLA; ++p)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          ka[p][b] = *reinterpret_cast<const i32x4*>(kt + (kbase ^ piece_xor(p)) + 32 * b * RB);
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        if (p + KLA < NP) {
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+            ka[(p + KLA) % (KLA + 1)][b] =
+                *reinterpret_cast<const i32x4*>(kt + (kbase ^ piece_xor(p + KLA)) + 32 * b * RB);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          s[b] = mfma_bf16(__builtin_bit_cast(bf16x8, ka[p % (KLA + 1)][b]), __builtin_bit_cast(bf16x8, qf[p]), s[b]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  // ---- X(j): mask, row max, conditional rescale, P_j = exp2(S_j sc - m), row sums ----
+  auto softmax_phase = [&](int j) __attribute__((always_inline)) {
+    if (j < 0 || j >= n_live) return;
+    const int key0 = ts.at(j) * BN;
+    // key key0 + 4h + r of the tile (r = 32b + 8(v/4) + v%4) is kept iff lo <= r <= hi
+    if (kb.mask_tile<BN>(key0, qw)) {
+      int hi = kb.hi(qrow) - key0 - 4 * hf, lo = kb.lo(qrow) - key0 - 4 * hf;
+      opaque(hi);
+      opaque(lo);
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = 32 * b + (v >> 2) * 8 + (v & 3);
+          if (r > hi || r < lo) s[b][v] = -INFINITY;
+        }
+    }
+    float m2[2] = {-INFINITY, -INFINITY};
+#pragma unroll
+    for (int kc = 0; kc < NC; ++kc) {
+      const f32x16& sv = s[kc >> 1];
+      const int o = (kc & 1) * 8;
+#pragma unroll
+      for (int v = 0; v < 8; v += 2) m2[kc & 1] = fmaxf(fmaxf(m2[kc & 1], sv[o + v]), sv[o + v + 1]);
+    }
+    const float mx = pair_max32(fmaxf(m2[0], m2[1])) * sc;
+    const bool grow = mx > m_ref + tau;
+    if (wave_any(grow)) {
+      const float m_new = grow ? mx : m_ref;
+      // rows that do not grow keep their scale (also when m_ref is still -inf: -inf - -inf is NaN)
+      const float alpha = grow ? fast_exp2(m_ref - m_new) : 1.f;
+      m_ref = m_new;
+      l_part *= alpha;
+#pragma unroll
+      for (int e = 0; e < NE; ++e) acc[e] *= alpha;
+    }
+    // a row that has kept no key yet (m_ref = -inf, only under a window) gets p = 2^-inf = 0
+    const float neg_m = m_ref == -INFINITY ? 0.f : -m_ref;
+    float l4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < NC; ++kc) {
+      f32x16& sv = s[kc >> 1];
+      const int o8 = (kc & 1) * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sv[o8 + i] = fast_exp2(__builtin_fmaf(sv[o8 + i], sc, neg_m));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pb[kc][i] = (__bf16)sv[o8 + i];
+      const i32x4 pw = __builtin_bit_cast(i32x4, pb[kc]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) l4[i] = dot2_bf16_sum(pw[i], l4[i]);
+    }
+    l_part += (l4[0] + l4[1]) + (l4[2] + l4[3]);
+  };
+
+  // The step loop, instantiated once per wave group so that each copy has a
+  // fixed phase order (SECOND: X(j-1) then M(j); else M(j) then X(j)).
+  auto run = [&](auto group) __attribute__((always_inline)) {
+    constexpr bool SECOND = decltype(group)::value;
+    // One step: K_{j+1} and V_j in flight, then this group's two phases.
+    auto step = [&](int j, const char* __restrict__ kcur, const char* __restrict__ vprev, char* __restrict__ knxt,
+                    char* __restrict__ vnxt) __attribute__((always_inline)) {
+      if (j + 1 < n_tiles) issue_k(ts.at(j + 1) * BN, knxt);
+      if (j < n_tiles) issue_v(ts.at(j) * BN, vnxt);
+      opaque(kbase);
+      opaque(vbase);
+      if constexpr (SECOND) {
+        softmax_phase(j - 1);
+        exec_barrier();
+        __builtin_amdgcn_s_setprio(1);
+        mma_phase(j, kcur, vprev);
+        __builtin_amdgcn_s_setprio(0);
+      } else {
+        __builtin_amdgcn_s_setprio(1);
+        mma_phase(j, kcur, vprev);
+        __builtin_amdgcn_s_setprio(0);
+        exec_barrier();
+        softmax_phase(j);
+      }
+      wait_vmem();
+      __syncthreads();
+    };
+    if (n_tiles > 0) issue_k(ts.at(0) * BN, ks0);
+    wait_vmem();
+    __syncthreads();
+    for (int j = 0; j <= n_tiles; j += 2) {
+      step(j, ks0, vs1, ks1, vs0);
+      if (j + 1 <= n_tiles) step(j + 1, ks1, vs0, ks0, vs1);
+    }
+  };
+  if (second)
+    run(BoolTag<true>{});
+  else
+    run(BoolTag<false>{});
+
+  // ---- epilogue: O = acc / l, lse = ln(sum exp(s)); O = 0, lse = -inf for a row that kept no key ----
+  const float l_tot = pair_sum32(l_part);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qrow < N) {
+    __bf16* orow = reinterpret_cast<__bf16*>(hr.o) + (size_t)qrow * P.so.r;
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 o4 = {(__bf16)(acc[e][4 * g] * inv), (__bf16)(acc[e][4 * g + 1] * inv),
+                     (__bf16)(acc[e][4 * g + 2] * inv), (__bf16)(acc[e][4 * g + 3] * inv)};
+        *reinterpret_cast<bf16x4*>(orow + 32 * e + 8 * g + 4 * hf) = o4;
+      }
+    if (hf == 0) hr.lse[qrow] = (m_ref + __builtin_log2f(l_tot)) * kLn2;
+  }
+}
+
+template <class C>
+static hipError_t launch_fwd_pp(const FwdParams& p0, int B, int H, hipStream_t st) {
+  FwdParams p = p0;
+  p.n_qtiles = (p.N + C::BM - 1) / C::BM;
+  const long long grid = (long long)p.n_qtiles * B * H;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (p.sk.r == p.sv.r)
+    hipLaunchKernelGGL((fwd_pp_kernel<C, true>), dim3((unsigned)grid), dim3(C::NT), 0, st, p);
+  else
+    hipLaunchKernelGGL((fwd_pp_kernel<C, false>), dim3((unsigned)grid), dim3(C::NT), 0, st, p);
+  return hipGetLastError();
+}
+
 template <class C>
 static hipError_t launch_fwd_pipe(const FwdParams& p0, int B, int H, hipStream_t st) {
   FwdParams p = p0;
@@ -673,6 +954,8 @@ static hipError_t launch_fwd_direct(const FwdParams& p0, int B, int H, hipStream
 }
 
 // Parameter table: D -> (keys per tile BN, waves per workgroup, waves per SIMD).
+// bf16 at D = 128 also has the phase-alternating kernel (eight waves, 64-key
+// tiles) for the shapes where it is faster.
 // Chosen so that two K/V stages fit LDS and, where registers allow, two
 // workgroups share a CU (one wave's softmax overlaps the other's MFMAs).
 hipError_t fwd_dispatch(Elt e, int D, const FwdParams& p, int B, int H, hipStream_t st) {
@@ -684,7 +967,14 @@ hipError_t fwd_dispatch(Elt e, int D, const FwdParams& p, int B, int H, hipStrea
       break;
     case Elt::BF16:
       if (D == 64) return launch_fwd_pipe<FwdDCfg<Elt::BF16, 64, 64, 4, 2>>(p, B, H, st);
-      if (D == 128) return launch_fwd_pipe<FwdDCfg<Elt::BF16, 128, 64, 4, 2>>(p, B, H, st);
+      if (D == 128) {
+        // the phase-alternating kernel where it measured faster: one query head
+        // per K/V head, no window, fixed lengths and no block list (its 256-row
+        // query tiles lose to 128-row ones on GQA and sliding windows)
+        if (!p.kv_index && !p.cu_q && p.window < 0 && p.group == 1)
+          return launch_fwd_pp<FwdPPCfg<128, 64>>(p, B, H, st);
+        return launch_fwd_pipe<FwdDCfg<Elt::BF16, 128, 64, 4, 2>>(p, B, H, st);
+      }
       if (D == 256) return launch_fwd_pipe<FwdDCfg<Elt::BF16, 256, 64, 4, 1>>(p, B, H, st);
       break;
     case Elt::FP8:
