@@ -20,6 +20,10 @@ counters recorded in profiles/traffic_bwd_dkdv.json, scaled by the same
 counters' reading for a plain copy kernel of known size (--calibrate-copy);
 it is reported only while the kernel sources still hash to the recorded value.
 
+The defaults (W = K = 200, about 0.15 s of GPU work) let the GPU reach its
+sustained clock before the timed steps: with 5 warm-up steps the first timed
+steps ran at a lower clock and the step read about 15% slower.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-breakdown]
        python bench.py --calibrate-copy    (plain 512 MiB device copy, for counter calibration)
 """
@@ -44,8 +48,8 @@ PEAK_HBM_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -152,12 +156,21 @@ def device_inputs(w, with_grad, shape=None):
     return out
 
 
-def time_fn(fn, iters, warmup=3):
-    """Average milliseconds per call of `fn` (launches on torch's current stream), by HIP events."""
+def time_fn(fn, iters, warmup=3, warm_ms=50.0):
+    """Average milliseconds per call of `fn` (launches on torch's current stream), by HIP events.
+
+    Untimed calls first: at least `warmup` of them and at least `warm_ms` of wall time, so that a
+    GPU left idle by host work (input generation, the CPU baseline) is back at its sustained clock.
+    """
     import torch
 
-    for _ in range(warmup):
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or (time.perf_counter() - t0) * 1e3 < warm_ms:
         fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
