@@ -9,6 +9,7 @@ exception is raised.
 from __future__ import annotations
 
 import ctypes
+import functools
 import math
 import os
 from typing import Optional, Tuple
@@ -145,6 +146,43 @@ def _dense(*ts) -> bool:
     return all(t is None or t.is_contiguous() for t in ts)
 
 
+def _check_like(t: torch.Tensor, shape, dtype, device, name: str, contiguous: bool = True):
+    """A caller-supplied tensor that a kernel reads or writes through a raw pointer: the C ABI sees only the
+    pointer, so its shape, dtype and device must be exactly the expected ones (else a kernel would run past its
+    end). `contiguous`: the whole tensor contiguous; otherwise its last dimension."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device:
+        raise ValueError(f"{name} must be a {dtype} tensor of shape {tuple(shape)} on {device} "
+                         f"(got {t.dtype} {tuple(t.shape)} on {t.device})")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not contiguous and t.dim() > 0 and t.stride(-1) != 1:
+        raise ValueError(f"{name} must have its last dimension contiguous")
+
+
+def _workspace(workspace: Optional[torch.Tensor], need: int, device) -> torch.Tensor:
+    if workspace is None:
+        return torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    if workspace.dtype != torch.uint8 or workspace.device != device or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous uint8 tensor on {device}")
+    return workspace
+
+
+def _on_device(fn):
+    """Run a binding with the device of its first tensor argument current (the kernels launch on that
+    device's current torch stream)."""
+
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        t = args[0] if args else None
+        if isinstance(t, torch.Tensor) and t.is_cuda:
+            with torch.cuda.device(t.device):
+                return fn(*args, **kwargs)
+        return fn(*args, **kwargs)
+
+    return wrapper
+
+
+@_on_device
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False, scale: Optional[float] = None,
         rescale_log2: Optional[float] = None, out: Optional[torch.Tensor] = None,
         lse: Optional[torch.Tensor] = None, window: Optional[int] = None,
@@ -163,15 +201,18 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
     Hkv, Nk = k.shape[1], k.shape[2]
     code = _dtype_code(q)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    odt = torch.float32 if code == FA_F32 else torch.bfloat16
     if out is None:
-        out = torch.empty(q.shape, dtype=torch.float32 if code == FA_F32 else torch.bfloat16, device=q.device)
+        out = torch.empty(q.shape, dtype=odt, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_like(out, q.shape, odt, q.device, "out", contiguous=dense)
+    _check_like(lse, (B, H, N), torch.float32, q.device, "lse", contiguous=dense)
     if block_lists is not None:
         if not dense or rescale_log2 is not None:
             raise ValueError("block-sparse calls take contiguous tensors and the default rescale threshold")
         bl = block_lists
-        bl.check(B, H, N, Nk, causal, window)
+        bl.check(B, H, N, Nk, causal, window, q.device)
         _check(lib().fa_fwd_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,
                                    Hkv, N, Nk, D, int(causal), -1 if window is None else int(window), scale, code,
                                    bl.kv_count.data_ptr(), bl.kv_index.data_ptr(), _stream(q)))
@@ -179,8 +220,6 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
     if not dense:
         if rescale_log2 is not None:
             raise ValueError("rescale_log2 is only taken with contiguous tensors")
-        if out.shape != q.shape or lse.shape != (B, H, N):
-            raise ValueError("out must be shaped like q and lse [B, H, N]")
         _check(lib().fa_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,
                                     Hkv, N, Nk, D, int(causal), -1 if window is None else int(window), scale, code,
                                     _strides(q, k, v, out, lse=lse), _stream(q)))
@@ -207,6 +246,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
     return out, lse
 
 
+@_on_device
 def fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False, scale: Optional[float] = None,
             q_descale: Optional[torch.Tensor] = None, k_descale: Optional[torch.Tensor] = None,
             v_descale: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
@@ -219,12 +259,14 @@ def fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_like(out, q.shape, torch.bfloat16, q.device, "out")
+    _check_like(lse, (B, H, N), torch.float32, q.device, "lse")
 
     def ptr(t):
         if t is None:
             return None
-        if t.dtype != torch.float32 or not t.is_cuda or t.numel() < 1:
-            raise ValueError("descales must be float32 device tensors with one element")
+        if t.dtype != torch.float32 or t.device != q.device or t.numel() < 1:
+            raise ValueError("descales must be float32 tensors on q's device with one element")
         return t.data_ptr()
 
     _check(lib().fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, D,
@@ -232,6 +274,7 @@ def fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
     return out, lse
 
 
+@_on_device
 def quantize_fp8(x: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
     """Per-tensor e4m3 quantisation of a float32 device tensor: returns (codes uint8, descale float32[1])."""
     if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
@@ -246,6 +289,7 @@ def bwd_workspace_size(B: int, H: int, N: int, D: int, variant: int = FA_BWD_ATO
     return int(lib().fa_bwd_workspace_size(B, H, N, D, FA_BF16, variant))
 
 
+@_on_device
 def bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None, variant: int = FA_BWD_ATOMIC,
         workspace: Optional[torch.Tensor] = None, dq=None, dk=None, dv=None, window: Optional[int] = None,
         block_lists: Optional["BlockLists"] = None):
@@ -257,19 +301,18 @@ def bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None
     B, H, N, D = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    if lse.dtype != torch.float32 or lse.shape != (B, H, N):
-        raise ValueError("lse must be float32 [B, H, N]")
-    need = bwd_workspace_size(B, H, N, D, variant)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_like(lse, (B, H, N), torch.float32, q.device, "lse", contiguous=dense)
+    workspace = _workspace(workspace, bwd_workspace_size(B, H, N, D, variant), q.device)
     dq = torch.empty(q.shape, dtype=q.dtype, device=q.device) if dq is None else dq
     dk = torch.empty(k.shape, dtype=k.dtype, device=k.device) if dk is None else dk
     dv = torch.empty(v.shape, dtype=v.dtype, device=v.device) if dv is None else dv
+    for t, like, name in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        _check_like(t, like.shape, q.dtype, q.device, name, contiguous=dense)
     if block_lists is not None:
         if not dense:
             raise ValueError("block-sparse calls take contiguous tensors")
         bl = block_lists
-        bl.check(B, H, N, Nk, causal, window)
+        bl.check(B, H, N, Nk, causal, window, q.device)
         _check(lib().fa_bwd_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
                                    lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, Nk, D,
                                    int(causal), -1 if window is None else int(window), scale, _dtype_code(q),
@@ -277,9 +320,6 @@ def bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None
                                    bl.q_index.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(q)))
         return dq, dk, dv
     if not dense:
-        for t, like in ((dq, q), (dk, k), (dv, v)):
-            if t.shape != like.shape or t.stride(-1) != 1:
-                raise ValueError("gradients must be shaped like their inputs with D contiguous")
         _check(lib().fa_bwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
                                     lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, Nk, D,
                                     int(causal), -1 if window is None else int(window), scale, _dtype_code(q),
@@ -304,19 +344,19 @@ def bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None
     return dq, dk, dv
 
 
+@_on_device
 def bwd_dkdv(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None,
              workspace: Optional[torch.Tensor] = None, dk=None, dv=None):
     """dK and dV only (bf16), the key-tile pass of the backward. Returns (dK, dV)."""
     _check_qkv(q, k, v, o, do)
     B, H, N, D = q.shape
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    if lse.dtype != torch.float32 or lse.shape != (B, H, N) or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 [B, H, N]")
-    need = bwd_workspace_size(B, H, N, D, FA_BWD_DETERMINISTIC)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_like(lse, (B, H, N), torch.float32, q.device, "lse")
+    workspace = _workspace(workspace, bwd_workspace_size(B, H, N, D, FA_BWD_DETERMINISTIC), q.device)
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    _check_like(dk, k.shape, q.dtype, q.device, "dk")
+    _check_like(dv, v.shape, q.dtype, q.device, "dv")
     _check(lib().fa_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
                              dk.data_ptr(), dv.data_ptr(), B, H, N, D, int(causal), scale, _dtype_code(q),
                              workspace.data_ptr(), workspace.numel(), _stream(q)))
@@ -325,17 +365,18 @@ def bwd_dkdv(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] =
 
 def _check_varlen(q, k, v, cu_q, cu_k):
     for t in (q, k, v):
-        if t.dim() != 3 or not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
-            raise ValueError("packed tensors must be contiguous [total, heads, D] device tensors of one dtype")
+        if t.dim() != 3 or not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("packed tensors must be contiguous [total, heads, D] tensors of one dtype on one device")
     if k.shape != v.shape or k.shape[2] != q.shape[2] or q.shape[1] % k.shape[1]:
         raise ValueError("k, v must be [total_k, Hkv, D] with Hkv dividing q's heads")
     for c in (cu_q, cu_k):
-        if c.dtype != torch.int32 or not c.is_cuda or not c.is_contiguous() or c.dim() != 1:
-            raise ValueError("cu_seqlens must be contiguous int32 device tensors")
+        if c.dtype != torch.int32 or c.device != q.device or not c.is_contiguous() or c.dim() != 1:
+            raise ValueError("cu_seqlens must be contiguous int32 tensors on q's device")
     if cu_q.numel() != cu_k.numel() or cu_q.numel() < 2:
         raise ValueError("cu_seqlens_q and cu_seqlens_k must both have B + 1 >= 2 entries")
 
 
+@_on_device
 def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int, causal: bool = False,
                scale: Optional[float] = None, window: Optional[int] = None, out=None, lse=None):
     """Packed variable-length forward: q [total_q, H, D], k, v [total_k, Hkv, D], int32 offsets [B + 1].
@@ -346,9 +387,11 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqle
     B = cu_seqlens_q.numel() - 1
     code = _dtype_code(q)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    out = torch.empty(q.shape, dtype=torch.float32 if code == FA_F32 else torch.bfloat16, device=q.device) \
-        if out is None else out
+    odt = torch.float32 if code == FA_F32 else torch.bfloat16
+    out = torch.empty(q.shape, dtype=odt, device=q.device) if out is None else out
     lse = torch.empty((H, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_like(out, q.shape, odt, q.device, "out")
+    _check_like(lse, (H, Tq), torch.float32, q.device, "lse")
     _check(lib().fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H, Hkv, Tq, Tk,
                                int(max_seqlen_q), int(max_seqlen_k), D, int(causal),
@@ -356,6 +399,7 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqle
     return out, lse
 
 
+@_on_device
 def bwd_varlen(q, k, v, o, do, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
                causal: bool = False, scale: Optional[float] = None, window: Optional[int] = None,
                variant: int = FA_BWD_ATOMIC, workspace=None, dq=None, dk=None, dv=None):
@@ -366,12 +410,15 @@ def bwd_varlen(q, k, v, o, do, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: in
     Tk, Hkv = k.shape[0], k.shape[1]
     B = cu_seqlens_q.numel() - 1
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    need = bwd_workspace_size(1, H, Tq, D, variant)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_like(o, q.shape, q.dtype, q.device, "o")
+    _check_like(do, q.shape, q.dtype, q.device, "do")
+    _check_like(lse, (H, Tq), torch.float32, q.device, "lse")
+    workspace = _workspace(workspace, bwd_workspace_size(1, H, Tq, D, variant), q.device)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.zeros_like(k) if dk is None else dk
     dv = torch.zeros_like(v) if dv is None else dv
+    for t, like, name in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        _check_like(t, like.shape, q.dtype, q.device, name)
     _check(lib().fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
                                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cu_seqlens_q.data_ptr(),
                                cu_seqlens_k.data_ptr(), B, H, Hkv, Tq, Tk, int(max_seqlen_q), int(max_seqlen_k), D,
@@ -387,11 +434,14 @@ class BlockLists:
         self.kv_count, self.kv_index, self.q_count, self.q_index = kv_count, kv_index, q_count, q_index
         self.geometry = geometry
 
-    def check(self, B, H, Nq, Nk, causal, window):
+    def check(self, B, H, Nq, Nk, causal, window, device=None):
         if self.geometry != (B, H, Nq, Nk, bool(causal), -1 if window is None else int(window)):
             raise ValueError(f"block lists were built for {self.geometry}, not {(B, H, Nq, Nk, causal, window)}")
+        if device is not None and self.kv_index.device != device:
+            raise ValueError(f"block lists live on {self.kv_index.device}, the tensors on {device}")
 
 
+@_on_device
 def block_lists(mask: torch.Tensor, Nq: int, Nk: int, causal: bool = False, window: Optional[int] = None
                 ) -> BlockLists:
     """Block lists of a [B, H, ceil(Nq / 128), ceil(Nk / 128)] mask (bool or uint8 device tensor, the last
