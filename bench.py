@@ -61,29 +61,22 @@ TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_bwd_dkdv.json")
 MFMA_RECORD = os.path.join(ROOT, "profiles", "mfma_util_step.json")
 
 
-def sources_sha256():
-    """Hash of the dominant kernel's sources with comments and blank lines removed (code changes only)."""
-    import hashlib
-    import re
-
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f)) as fh:
-            text = re.sub(r"//[^\n]*", "", fh.read())
-        h.update("\n".join(l.rstrip() for l in text.splitlines() if l.strip()).encode())
-    return h.hexdigest()
-
-
-def _hash_files(paths):
+def _hash_files(paths, root=ROOT):
+    """sha256 of the files' code: `//` comments, trailing blanks and blank lines removed."""
     import hashlib
     import re
 
     h = hashlib.sha256()
     for f in paths:
-        with open(os.path.join(ROOT, f)) as fh:
+        with open(os.path.join(root, f)) as fh:
             text = re.sub(r"//[^\n]*", "", fh.read())
         h.update("\n".join(l.rstrip() for l in text.splitlines() if l.strip()).encode())
     return h.hexdigest()
+
+
+def sources_sha256():
+    """Hash of the dominant kernel's sources with comments and blank lines removed (code changes only)."""
+    return _hash_files(KERNEL_SOURCES)
 
 
 def step_sources_sha256():
@@ -103,7 +96,8 @@ def recorded_mfma():
         return None
     out = {}
     for k, v in rec["kernels"].items():
-        key = next((n for n in ("fwd_pipe_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel", "bwd_pre_kernel") if n in k), k)
+        key = next((n for n in ("fwd_pipe_kernel", "fwd_pp_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel",
+                                "bwd_pre_kernel") if n in k), k)
         out[key] = {"mfma_util_pct": round(v["mfma_util_pct"], 1), "hbm_gbps": round(v["hbm_gbps"] or 0.0, 1)}
     return {"kernels": out, "source": "profiles/mfma_util_mh_causal_b4h16n2048d128.md"}
 
