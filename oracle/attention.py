@@ -191,6 +191,35 @@ def backward(q, k, v, do, causal, scale, window=-1, block_mask=None, block=128):
     return dq, dk, dv
 
 
+def backward_dq_rows(q, k, v, do, causal, scale, rows, window=-1):
+    """dQ of the listed query rows only, in float64 (for heads too long to materialise S).
+
+    dQ_i depends on row i alone: with s_i = scale q_i K^T over the kept keys,
+    p_i = softmax(s_i), dp_i = dO_i V^T and ds_i = p_i * (dp_i - <p_i, dp_i>),
+    dQ_i = scale ds_i K -- the row-i slice of ``backward``'s dQ, the same chain
+    rule. rows: sorted 1-D array of query indices. Returns [B, H, len(rows), D].
+    """
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    do = _as_f64(do)
+    B, H, N, D = q.shape
+    G = _group(H, k.shape[1])
+    sel = np.asarray(rows, dtype=np.int64)
+    dq = np.empty((B, H, len(sel), D))
+    for b in range(B):
+        for h in range(H):
+            kh = h // G
+            for r0, r1 in _row_blocks(len(sel), k.shape[2]):
+                rr = sel[r0:r1]
+                s = scores(q[b, h, rr], k[b, kh], scale, causal, rows=rr, n_q=N, window=window)
+                p, _ = softmax_rows(s)
+                dp = do[b, h, rr] @ v[b, kh].T
+                ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+                dq[b, h, r0:r1] = scale * (ds @ k[b, kh])
+    return dq
+
+
 def _check_cu(cu, total, B):
     cu = np.asarray(cu, dtype=np.int64)
     if cu.shape != (B + 1,) or cu[0] != 0 or cu[-1] != total or np.any(np.diff(cu) < 0):

@@ -560,3 +560,36 @@ def pin_block_mask_brute(fwd, bwd, brute, tol=1e-12):
                              window=w, block_mask=ml, block=block)
         for a, b in zip(g, g_b):
             np.testing.assert_allclose(a[0, 0], np.array(b), atol=tol)
+
+
+def pin_dq_rows_brute(dq_rows, brute, tol=1e-12):
+    """The row-sampled dQ against pure-Python loops on N <= 16 (causal, window, N_q != N_k)."""
+    for (nq, nk, causal, window, seed) in [(9, 9, False, -1, 80), (12, 7, True, -1, 81), (6, 14, True, 3, 82),
+                                           (16, 16, True, 0, 83)]:
+        q, do = (_rand((1, 1, nq, 5), seed + i) for i in range(2))
+        k, v = (_rand((1, 1, nk, 5), seed + 2 + i) for i in range(2))
+        rows = np.array(sorted({0, nq // 2, nq - 1}))
+        got = dq_rows(q, k, v, do, causal, 0.8, rows, window=window)
+        bdq, _, _ = brute.backward(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), do[0, 0].tolist(), causal,
+                                   0.8, window=window)
+        np.testing.assert_allclose(got[0, 0], np.array(bdq)[rows], atol=tol)
+
+
+def pin_dq_rows_torch(dq_rows, tol=1e-11):
+    """The row-sampled dQ against torch CPU float64 autograd of the plain formula (GQA, bottom-right causal)."""
+    import torch
+
+    B, H, Hkv, nq, nk, D = 2, 4, 2, 20, 33, 8
+    q, do = (_rand((B, H, nq, D), 90 + i) for i in range(2))
+    k, v = (_rand((B, Hkv, nk, D), 92 + i) for i in range(2))
+    rows = np.array([0, 3, 11, 19])
+    got = dq_rows(q, k, v, do, True, 0.45, rows)
+    tq = torch.from_numpy(q).requires_grad_(True)
+    tk = torch.from_numpy(k).repeat_interleave(H // Hkv, dim=1)
+    tv = torch.from_numpy(v).repeat_interleave(H // Hkv, dim=1)
+    s = 0.45 * (tq @ tk.transpose(-1, -2))
+    i = torch.arange(nq)[:, None]
+    j = torch.arange(nk)[None, :]
+    s = s.masked_fill(j > i + (nk - nq), float("-inf"))
+    (torch.softmax(s, dim=-1) @ tv * torch.from_numpy(do)).sum().backward()
+    np.testing.assert_allclose(got, tq.grad.numpy()[:, :, rows], atol=tol)

@@ -114,3 +114,11 @@ def test_block_mask_drops_keys():
 
 def test_block_mask_brute():
     pins.pin_block_mask_brute(attention.forward, attention.backward, brute)
+
+
+def test_dq_rows_brute():
+    pins.pin_dq_rows_brute(attention.backward_dq_rows, brute)
+
+
+def test_dq_rows_torch():
+    pins.pin_dq_rows_torch(attention.backward_dq_rows)

@@ -404,3 +404,46 @@ def test_unmutated_block_factory_passes():
     pins.pin_block_mask_torch(fwd, bwd)
     pins.pin_block_mask_drops_keys(fwd)
     pins.pin_block_mask_brute(fwd, bwd, brute)
+
+
+def _dq_rows_factory(mutant=None):
+    """Copies of the row-sampled dQ with one planted mistake each."""
+
+    def dq_rows(q, k, v, do, causal, scale, rows, window=-1):
+        q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+        B, H, N, D = q.shape
+        G = H // k.shape[1]
+        rows = np.asarray(rows)
+        src = np.minimum(rows + 1, N - 1) if mutant == "row_shift" else rows
+        out = np.empty((B, H, len(rows), D))
+        for b in range(B):
+            for h in range(H):
+                kk, vv = k[b, h // G], v[b, h // G]
+                n_q = N if mutant != "top_left" else kk.shape[0]
+                s = attention.scores(q[b, h, src], kk, scale, causal, rows=src, n_q=n_q, window=window)
+                p, _ = attention.softmax_rows(s)
+                dp = do[b, h, src] @ vv.T
+                c = 0.0 if mutant == "no_jacobian" else (p * dp).sum(axis=1, keepdims=True)
+                ds = p * (dp - c)
+                out[b, h] = (1.0 if mutant == "no_scale" else scale) * (ds @ kk)
+        return out
+
+    return dq_rows
+
+
+@pytest.mark.parametrize("mutant", ["row_shift", "top_left", "no_jacobian", "no_scale"])
+def test_dq_rows_mutants_fail_a_pin(mutant):
+    f = _dq_rows_factory(mutant)
+    failures = 0
+    for pin in (lambda: pins.pin_dq_rows_brute(f, brute), lambda: pins.pin_dq_rows_torch(f)):
+        try:
+            pin()
+        except AssertionError:
+            failures += 1
+    assert failures > 0, mutant
+
+
+def test_unmutated_dq_rows_factory_passes():
+    f = _dq_rows_factory()
+    pins.pin_dq_rows_brute(f, brute)
+    pins.pin_dq_rows_torch(f)
