@@ -721,10 +721,11 @@ bool bwd_supported(int D) { return D == 64 || D == 128; }
 // tile, waves per SIMD). The atomic pass holds a K tile and a dS^T tile in LDS
 // on top of the stages, so it runs one workgroup per CU with larger query tiles;
 // the plain key pass uses 32-query tiles, which fit three waves per SIMD at
-// D=64 and two at D=128.
+// D=64 and two at D=128; the D=64 dQ pass likewise takes 32-key tiles to run
+// three waves per SIMD.
 hipError_t bwd_dispatch(int D, int variant, const BwdParams& p, int B, int H, hipStream_t st) {
   if (D == 64)
-    return launch_bwd<DkdvCfg<64, 4, 64, 2>, DkdvCfg<64, 4, 32, 3>, DqCfg<64, 4, 64, 2>>(variant, p, B, H, st);
+    return launch_bwd<DkdvCfg<64, 4, 64, 2>, DkdvCfg<64, 4, 32, 3>, DqCfg<64, 4, 32, 3>>(variant, p, B, H, st);
   if (D == 128)
     return launch_bwd<DkdvCfg<128, 4, 64, 1>, DkdvCfg<128, 4, 32, 2>, DqCfg<128, 4, 64, 2>>(variant, p, B, H, st);
   return hipErrorInvalidValue;
