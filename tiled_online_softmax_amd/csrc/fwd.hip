@@ -978,8 +978,9 @@ hipError_t fwd_dispatch(Elt e, int D, const FwdParams& p, int B, int H, hipStrea
       if (D == 256) return launch_fwd_pipe<FwdDCfg<Elt::BF16, 256, 64, 4, 1>>(p, B, H, st);
       break;
     case Elt::FP8:
-      if (D == 64) return launch_fwd_direct<FwdDCfg<Elt::FP8, 64, 64, 4, 2>>(p, B, H, st);
-      if (D == 128) return launch_fwd_direct<FwdDCfg<Elt::FP8, 128, 64, 4, 2>>(p, B, H, st);
+      // e4m3 operands need few registers (105 / 154 VGPRs): four and three waves per SIMD
+      if (D == 64) return launch_fwd_direct<FwdDCfg<Elt::FP8, 64, 64, 4, 4>>(p, B, H, st);
+      if (D == 128) return launch_fwd_direct<FwdDCfg<Elt::FP8, 128, 64, 4, 3>>(p, B, H, st);
       break;
   }
   return hipErrorInvalidValue;
