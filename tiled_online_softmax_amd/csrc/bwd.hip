@@ -12,7 +12,9 @@
 //   * deterministic: the same key-tile pass for dK and dV, plus a second pass
 //     over query tiles that recomputes S and dP to form dQ -- 7 matrix
 //     products instead of 5 and no atomics, parallel over both rows and
-//     columns of the attention matrix.
+//     columns of the attention matrix. The query-tile pass runs first and
+//     also writes the row statistics the key-tile pass reads (it holds each
+//     query row's dO anyway), so this variant needs no preprocess kernel.
 //
 // CDNA4 mapping. The key-tile kernel computes S = Q K^T with 32x32 MFMAs so a
 // lane holds one key's scores for 16 queries: dV^T += dO^T P and
@@ -33,7 +35,9 @@ constexpr float kInf = __builtin_huge_valf();
 // Row statistics for the passes: ld[row] = lse * log2(e) and
 // ld[rows + row] = -D with D = sum_d dO O (negated so it can initialise the
 // dP accumulator, which then holds dP - D for free); the atomic variant also
-// zeroes dQ_accum. One thread per 8 consecutive elements of a row.
+// zeroes dQ_accum. One thread per 8 consecutive elements of a row. (The
+// deterministic variant's dQ pass computes the same values, in the same
+// order, for its own rows.)
 //
 // Workspace row r = (b * H + h) * Np + i is query row i of head h of entry b
 // (packed sequences: Bp = 1 and i runs over all packed rows, which is the
@@ -495,11 +499,42 @@ bwd_dq_kernel(BwdParams P, int n_qtiles) {
     qf[p] = buf_load16(rq, (uint32_t)qrow * qrs + 32 * p + 16 * hf);
     dof[p] = buf_load16(rdo, (uint32_t)qrow * dors + 32 * p + 16 * hf);
   }
-  float lse_l2 = kInf, dlt = 0.f;
+  // Row statistics of this lane's query row, written to the workspace for the
+  // key-tile pass that runs after this one: lse * log2(e) and D = <dO, O>,
+  // summed as bwd_pre_kernel sums them (8-element pieces, then pairs of
+  // pieces 8, 4, 2, 1 apart; piece 2p + hf is this lane's piece p), so both
+  // paths give bitwise the same values.
+  const __bf16* oh = static_cast<const __bf16*>(P.o) + (bb * P.so.b + h * P.so.h + sq.tq * P.so.r);
+  const uint32_t ors = (uint32_t)(P.so.r * 2);
+  const auto ro = make_rsrc(oh, head_span(N, ors, RB));
+  float dpart[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const bf16x8 ov = __builtin_bit_cast(bf16x8, buf_load16(ro, (uint32_t)qrow * ors + 32 * p + 16 * hf));
+    const bf16x8 dv8 = __builtin_bit_cast(bf16x8, dof[p]);
+    float t = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t += (float)ov[j] * (float)dv8[j];
+    dpart[p] = t;
+  }
+#pragma unroll
+  for (int m = NP / 2; m >= 1; m >>= 1) {
+    float t[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) t[p] = dpart[p] + dpart[p ^ m];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) dpart[p] = t[p];
+  }
+  const float dlt = pair_sum32(dpart[0]);
+  float lse_l2 = kInf;
   if (qrow < N) {
     const size_t r = (size_t)(bb * P.ld_b + h * P.ld_h + sq.tq) + qrow;  // workspace row
-    lse_l2 = P.ld[r];
-    dlt = -P.ld[(size_t)P.rows + r];
+    const float l = P.lse[bb * P.lse_b + h * P.lse_h + sq.tq + qrow];
+    lse_l2 = l == -kInf ? kInf : l * kLog2e;
+    if (hf == 0) {
+      P.ld[r] = lse_l2;
+      P.ld[(size_t)P.rows + r] = -dlt;
+    }
   }
   const float sl2 = P.scale_log2;
 
@@ -673,44 +708,44 @@ static hipError_t launch_bwd(int variant, const BwdParams& p, int B, int H, hipS
   const int HKV = H / p.group;  // the key-tile passes run over K/V heads
   // Q/dO equally spaced and workspace rows of every query tile 16-byte aligned
   const bool plain = p.sq.r == p.sdo.r && !p.cu_q && p.N % 4 == 0;
-  hipError_t e = launch_pre<KCD::D>(p, H, st);
-  if (e != hipSuccess) return e;
-  if (variant == 0) {
-    const int nk = (p.Nk + KCA::BK - 1) / KCA::BK;
-    const long long gk = (long long)nk * B * HKV;
-    if (gk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    if (p.q_index)  // block-sparse
-      hipLaunchKernelGGL((bwd_dkdv_kernel<KCA, true, false, true>), dim3((unsigned)gk), dim3(KCA::NT), 0, st, p, nk);
-    else if (plain)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<KCA, true, true, false>), dim3((unsigned)gk), dim3(KCA::NT), 0, st, p, nk);
+  // every grid is checked before anything is launched
+  const int nka = (p.Nk + KCA::BK - 1) / KCA::BK, nkd = (p.Nk + KCD::BK - 1) / KCD::BK;
+  const int nq = (p.N + QC::BM - 1) / QC::BM;
+  const long long gka = (long long)nka * B * HKV, gkd = (long long)nkd * B * HKV, gq = (long long)nq * B * H;
+  if ((variant == 0 ? gka : gkd) > 0x7fffffffLL || (variant == 1 && gq > 0x7fffffffLL))
+    return hipErrorInvalidConfiguration;
+  hipError_t e;
+  if (variant == 1) {
+    // dQ pass first: it also writes the row statistics the key-tile pass reads
+    if (p.kv_index)  // block-sparse calls take contiguous layouts
+      hipLaunchKernelGGL((bwd_dq_kernel<QC, true, true>), dim3((unsigned)gq), dim3(QC::NT), 0, st, p, nq);
+    else if (p.sk.r == p.sv.r)
+      hipLaunchKernelGGL((bwd_dq_kernel<QC, true, false>), dim3((unsigned)gq), dim3(QC::NT), 0, st, p, nq);
     else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<KCA, true, false, false>), dim3((unsigned)gk), dim3(KCA::NT), 0, st, p, nk);
+      hipLaunchKernelGGL((bwd_dq_kernel<QC, false, false>), dim3((unsigned)gq), dim3(QC::NT), 0, st, p, nq);
+  } else if ((e = launch_pre<KCD::D>(p, H, st)) != hipSuccess) {
+    return e;
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (variant == 0) {
+    if (p.q_index)  // block-sparse
+      hipLaunchKernelGGL((bwd_dkdv_kernel<KCA, true, false, true>), dim3((unsigned)gka), dim3(KCA::NT), 0, st, p, nka);
+    else if (plain)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<KCA, true, true, false>), dim3((unsigned)gka), dim3(KCA::NT), 0, st, p, nka);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<KCA, true, false, false>), dim3((unsigned)gka), dim3(KCA::NT), 0, st, p, nka);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int Np = p.cu_q ? p.total_q : p.N, nb = row_blocks<KCA::D>(Np);
     hipLaunchKernelGGL(bwd_dq_convert_kernel<KCA::D>, dim3((unsigned)((long long)nb * (p.rows / Np))), dim3(256), 0,
                        st, p, H, Np, nb);
     return hipGetLastError();
   }
-  const int nk = (p.Nk + KCD::BK - 1) / KCD::BK;
-  const long long gk = (long long)nk * B * HKV;
-  if (gk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (p.q_index)  // block-sparse
-    hipLaunchKernelGGL((bwd_dkdv_kernel<KCD, false, false, true>), dim3((unsigned)gk), dim3(KCD::NT), 0, st, p, nk);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<KCD, false, false, true>), dim3((unsigned)gkd), dim3(KCD::NT), 0, st, p, nkd);
   else if (plain)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<KCD, false, true, false>), dim3((unsigned)gk), dim3(KCD::NT), 0, st, p, nk);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<KCD, false, true, false>), dim3((unsigned)gkd), dim3(KCD::NT), 0, st, p, nkd);
   else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<KCD, false, false, false>), dim3((unsigned)gk), dim3(KCD::NT), 0, st, p, nk);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (variant == 2) return hipSuccess;  // dK/dV only
-  const int nq = (p.N + QC::BM - 1) / QC::BM;
-  const long long gq = (long long)nq * B * H;
-  if (gq > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  if (p.kv_index)  // block-sparse calls take contiguous layouts
-    hipLaunchKernelGGL((bwd_dq_kernel<QC, true, true>), dim3((unsigned)gq), dim3(QC::NT), 0, st, p, nq);
-  else if (p.sk.r == p.sv.r)
-    hipLaunchKernelGGL((bwd_dq_kernel<QC, true, false>), dim3((unsigned)gq), dim3(QC::NT), 0, st, p, nq);
-  else
-    hipLaunchKernelGGL((bwd_dq_kernel<QC, false, false>), dim3((unsigned)gq), dim3(QC::NT), 0, st, p, nq);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<KCD, false, false, false>), dim3((unsigned)gkd), dim3(KCD::NT), 0, st, p, nkd);
   return hipGetLastError();
 }
 
