@@ -285,15 +285,18 @@ def quantize_fp8(x: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
     return codes, descale
 
 
-def bwd_workspace_size(B: int, H: int, N: int, D: int, variant: int = FA_BWD_ATOMIC) -> int:
+def bwd_workspace_size(B: int, H: int, N: int, D: int, variant: int = FA_BWD_DETERMINISTIC) -> int:
     return int(lib().fa_bwd_workspace_size(B, H, N, D, FA_BF16, variant))
 
 
 @_on_device
-def bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None, variant: int = FA_BWD_ATOMIC,
+def bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None, variant: int = FA_BWD_DETERMINISTIC,
         workspace: Optional[torch.Tensor] = None, dq=None, dk=None, dv=None, window: Optional[int] = None,
         block_lists: Optional["BlockLists"] = None):
     """Attention backward (bf16). Returns (dQ, dK, dV) as bf16 tensors; dK, dV have k's shape.
+
+    The default variant is the atomics-free one: bitwise reproducible and, on MI355X, about twice as
+    fast as FA_BWD_ATOMIC (which needs no second pass over the keys but adds dQ with float atomics).
 
     Non-contiguous [B, H, N, D] views (D contiguous) go through fa_bwd_strided."""
     dense = _dense(q, k, v, o, do, dq, dk, dv, lse)
@@ -402,7 +405,7 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqle
 @_on_device
 def bwd_varlen(q, k, v, o, do, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
                causal: bool = False, scale: Optional[float] = None, window: Optional[int] = None,
-               variant: int = FA_BWD_ATOMIC, workspace=None, dq=None, dk=None, dv=None):
+               variant: int = FA_BWD_DETERMINISTIC, workspace=None, dq=None, dk=None, dv=None):
     """Gradients of fwd_varlen (bf16). Returns (dQ, dK, dV) in the packed layouts (new dK, dV are zeroed
     first: key rows outside every sequence are not written)."""
     _check_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k)
