@@ -35,6 +35,9 @@ namespace fa {
 // 32x32x2 MFMA contracts two keys held by the two lane halves). The tile loop is unrolled by two so the stage base of
 // every LDS read is an immediate.
 // ---------------------------------------------------------------------------
+// log2(448): e4m3's largest finite value is 448; P is encoded as e4m3(p * 448).
+constexpr float kLog2P8 = 8.80735492205760410744f;
+
 template <Elt E, int D_, int BN_, int NW_, int OCC_>
 struct FwdDCfg {
   static constexpr Elt elt = E;
@@ -90,11 +93,14 @@ fwd_kernel(FwdParams P) {
   if constexpr (C::elt == Elt::FP8) {
     // descales fold into the score scale and the output; P is encoded as
     // e4m3(p * 448), which needs p <= 1, hence rescaling on every increase.
+    // The exponent is offset by log2 448, so the exponentials yield p * 448
+    // directly; the float32 row sum then also carries the factor, which
+    // cancels in O and is taken out of lse.
     const float dq = P.q_descale ? *P.q_descale : 1.f;
     const float dk = P.k_descale ? *P.k_descale : 1.f;
     const float dv = P.v_descale ? *P.v_descale : 1.f;
     sc *= dq * dk;
-    out_mul = dv * (1.f / 448.f);
+    out_mul = dv;
     tau = 0.f;
   }
 
@@ -248,7 +254,7 @@ fwd_kernel(FwdParams P) {
         for (int e = 0; e < NE; ++e) acc[e] *= alpha;
       }
       // a row that has kept no key yet (m_ref = -inf, only under a window) gets p = 2^-inf = 0
-      const float neg_m = m_ref == -INFINITY ? 0.f : -m_ref;
+      const float neg_m = (m_ref == -INFINITY ? 0.f : -m_ref) + (C::elt == Elt::FP8 ? kLog2P8 : 0.f);
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -294,8 +300,8 @@ fwd_kernel(FwdParams P) {
             const f32x16& sb = s[2 * kc + (j >> 2)];
             const int o = (j & 3) * 4;
             l_part += (sb[o] + sb[o + 1]) + (sb[o + 2] + sb[o + 3]);
-            int w32 = cvt_fp8x2<false>(sb[o] * 448.f, sb[o + 1] * 448.f, 0);
-            w32 = cvt_fp8x2<true>(sb[o + 2] * 448.f, sb[o + 3] * 448.f, w32);
+            int w32 = cvt_fp8x2<false>(sb[o], sb[o + 1], 0);
+            w32 = cvt_fp8x2<true>(sb[o + 2], sb[o + 3], w32);
             pb[j] = w32;
           }
 #pragma unroll
@@ -357,7 +363,7 @@ fwd_kernel(FwdParams P) {
           *reinterpret_cast<bf16x4*>(orow + 32 * e + 8 * g + 4 * hf) = o4;
         }
     }
-    if (hf == 0) hr.lse[qrow] = (m_ref + __builtin_log2f(l_tot)) * kLn2;
+    if (hf == 0) hr.lse[qrow] = (m_ref + __builtin_log2f(l_tot) - (C::elt == Elt::FP8 ? kLog2P8 : 0.f)) * kLn2;
   }
 }
 
