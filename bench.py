@@ -24,7 +24,7 @@ The defaults (W = K = 200, about 0.15 s of GPU work) let the GPU reach its
 sustained clock before the timed steps: with 5 warm-up steps the first timed
 steps ran at a lower clock and the step read about 15% slower.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-breakdown]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-breakdown] [--breakdown-only]
        python bench.py --calibrate-copy    (plain 512 MiB device copy, for counter calibration)
 """
 from __future__ import annotations
@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--breakdown-only", action="store_true",
+                    help="time each workload's headline pass alone and print that JSON (no step line)")
     return ap.parse_args()
 
 
@@ -289,6 +291,9 @@ def main():
     from tiled_online_softmax_amd import fa, inputs
 
     fa.lib()
+    if args.breakdown_only:
+        print(json.dumps({"workloads": breakdown()}), flush=True)
+        return
     w = inputs.WORKLOADS["mh_causal_bf16"]
     x = device_inputs(w, with_grad=True)
     variant = fa.FA_BWD_DETERMINISTIC
