@@ -230,6 +230,15 @@ __device__ __forceinline__ uint32_t tr8_off(int lane, int e) {
 // count is a multiple of 8 * group, so their K/V tiles are fetched into one L2.
 // (Giving each XCD a contiguous block of heads instead raised the backward
 // key-tile pass's L2 misses by about half, with no change in its time.)
+// The forward's choice of order for a causal launch. A window that keeps every
+// row to at most a quarter of the n keys leaves all query tiles but a short
+// ramp at the start with the same cost, so the head-by-head order keeps each
+// head's K/V in one L2 without a long tail (1-3% faster forwards). The
+// backward passes measured slower that way and keep the rank-major order.
+__device__ __forceinline__ bool fwd_uneven_tiles(int causal, int window, int n) {
+  return causal && !(window >= 0 && 4LL * window <= n);
+}
+
 __device__ __forceinline__ void wg_map(int n_tiles, bool causal, int group, int& bh, int& rank) {
   const int G = gridDim.x, g = blockIdx.x;
   if (causal) {
