@@ -219,29 +219,36 @@ __device__ __forceinline__ uint32_t tr8_off(int lane, int e) {
 }
 
 // Workgroup -> (head, tile rank). blockIdx values are dealt round-robin to the
-// 8 XCDs in dispatch order. Without causal masking every tile costs the same:
-// each XCD gets a contiguous run of workgroups (whole heads when the tile count
-// allows), so the K/V of a head stay in one L2. Under causal masking the tiles
-// of a head cost from one to n_tiles units, and a head-by-head order leaves
-// long workgroups for the end of the launch; there the order is rank-major
+// 8 XCDs in dispatch order. Where every tile costs about the same: each XCD
+// gets a contiguous run of workgroups (whole heads when the tile count
+// allows), so the K/V of a head stay in one L2. Where costs are uneven
+// (`uneven`, chosen by rank_major): under causal masking the tiles of a head
+// cost from one to n_tiles units, and a head-by-head order leaves long
+// workgroups for the end of the launch; there the order is rank-major
 // (rank 0, the costliest tile, of every head first), which schedules the
 // longest workgroups first. The `group` consecutive heads that share one K/V
 // head stay on one XCD (whole groups u with u % 8 = x on XCD x) when the head
 // count is a multiple of 8 * group, so their K/V tiles are fetched into one L2.
 // (Giving each XCD a contiguous block of heads instead raised the backward
 // key-tile pass's L2 misses by about half, with no change in its time.)
-// The forward's choice of order for a causal launch. A window that keeps every
-// row to at most a quarter of the n keys leaves all query tiles but a short
-// ramp at the start with the same cost, so the head-by-head order keeps each
-// head's K/V in one L2 without a long tail (1-3% faster forwards). The
-// backward passes measured slower that way and keep the rank-major order.
-__device__ __forceinline__ bool fwd_uneven_tiles(int causal, int window, int n) {
-  return causal && !(window >= 0 && 4LL * window <= n);
+// Whether a launch takes wg_map's rank-major order. Packed sequences always
+// do: with the head-by-head order each XCD gets a contiguous run of whole
+// sequences, and with mixed lengths one XCD holds the longest (3x slower
+// forward and backward on 16 sequences of 17-4096 rows, and 2.4x on a windowed
+// forward). Otherwise causal launches do, except a forward whose window keeps
+// every row to at most a quarter of the n keys: all its query tiles but a short
+// ramp at the start cost the same, so the head-by-head order keeps each head's
+// K/V in one L2 without a long tail (1-3% faster). The backward passes
+// measured slower that way and keep the rank-major order under windows.
+__device__ __forceinline__ bool rank_major(bool packed, int causal, int window, int n, bool forward) {
+  if (packed) return true;
+  if (!causal) return false;
+  return !(forward && window >= 0 && 4LL * window <= n);
 }
 
-__device__ __forceinline__ void wg_map(int n_tiles, bool causal, int group, int& bh, int& rank) {
+__device__ __forceinline__ void wg_map(int n_tiles, bool uneven, int group, int& bh, int& rank) {
   const int G = gridDim.x, g = blockIdx.x;
-  if (causal) {
+  if (uneven) {
     const int BH = G / n_tiles;
     const int i = g % BH;
     if (BH % (8 * group) == 0) {
