@@ -140,7 +140,7 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
   // the query tiles of every head of the group, which sums their dK and dV
   // contributions in the accumulators.
   int bh, kt;
-  wg_map(n_ktiles, rank_major(P.cu_q != nullptr, P.causal, P.window, min(P.N, P.Nk), false), 1, bh, kt);
+  wg_map(n_ktiles, rank_major(P.cu_q != nullptr || P.kv_index != nullptr, P.causal, P.window, min(P.N, P.Nk), false), 1, bh, kt);
   const int group = P.group;
   const int hkv = P.hq / group;
   const int b = bh / hkv, hk = bh % hkv, h0 = hk * group;
@@ -469,7 +469,7 @@ bwd_dq_kernel(BwdParams P, int n_qtiles) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps per-wave branches scalar
 
   int bh, qt;
-  wg_map(n_qtiles, rank_major(P.cu_q != nullptr, P.causal, P.window, min(P.N, P.Nk), false), P.group, bh, qt);
+  wg_map(n_qtiles, rank_major(P.cu_q != nullptr || P.kv_index != nullptr, P.causal, P.window, min(P.N, P.Nk), false), P.group, bh, qt);
   const int b = bh / P.hq, h = bh % P.hq, hk = h / P.group;
   const Seq sq = seq_of(P.cu_q, P.cu_k, b, P.N, P.Nk, P.total_q, P.total_k);
   const int N = sq.nq;

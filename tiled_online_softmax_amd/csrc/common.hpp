@@ -231,17 +231,20 @@ __device__ __forceinline__ uint32_t tr8_off(int lane, int e) {
 // count is a multiple of 8 * group, so their K/V tiles are fetched into one L2.
 // (Giving each XCD a contiguous block of heads instead raised the backward
 // key-tile pass's L2 misses by about half, with no change in its time.)
-// Whether a launch takes wg_map's rank-major order. Packed sequences always
-// do: with the head-by-head order each XCD gets a contiguous run of whole
-// sequences, and with mixed lengths one XCD holds the longest (3x slower
-// forward and backward on 16 sequences of 17-4096 rows, and 2.4x on a windowed
-// forward). Otherwise causal launches do, except a forward whose window keeps
-// every row to at most a quarter of the n keys: all its query tiles but a short
-// ramp at the start cost the same, so the head-by-head order keeps each head's
-// K/V in one L2 without a long tail (1-3% faster). The backward passes
-// measured slower that way and keep the rank-major order under windows.
-__device__ __forceinline__ bool rank_major(bool packed, int causal, int window, int n, bool forward) {
-  if (packed) return true;
+// Whether a launch takes wg_map's rank-major order. Packed sequences and
+// block-sparse launches (`irregular`) always do: with the head-by-head order
+// each XCD gets a contiguous run of whole heads or sequences, and tiles of
+// very different cost end up bunched. Rank-major was 3x faster on 16 packed
+// sequences of 17-4096 rows, non-causal (forward and backward) and 2.4x on a
+// windowed packed forward. On a non-causal block-sparse backward it was 1.7x
+// faster, with the forward within 1%. Otherwise causal launches do, except
+// a forward whose window keeps every row to at most a quarter of the n keys:
+// all its query tiles but a short ramp at the start cost the same, so the
+// head-by-head order keeps each head's K/V in one L2 without a long tail (1-3%
+// faster). The backward passes measured slower that way and keep the
+// rank-major order under windows.
+__device__ __forceinline__ bool rank_major(bool irregular, int causal, int window, int n, bool forward) {
+  if (irregular) return true;
   if (!causal) return false;
   return !(forward && window >= 0 && 4LL * window <= n);
 }
