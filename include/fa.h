@@ -39,7 +39,7 @@
  * Errors: every entry point returns an fa_status. Arguments are validated
  * before any HIP call (so validation works without a GPU); on failure
  * fa_last_error() describes the problem. FA_ERR_INVALID_ARG: null pointer,
- * B/H/N/D < 1, scale negative or not finite, causal not 0/1, a pointer not
+ * B/H/N/D < 1, scale not > 0 or not finite, causal not 0/1, a pointer not
  * 16-byte aligned, or one head larger than 2^31 bytes. FA_ERR_UNSUPPORTED: D
  * not in the parameter table or a dtype/pass pair that is not built.
  * FA_ERR_WORKSPACE: workspace too small. FA_ERR_HIP: a HIP launch error
@@ -78,7 +78,7 @@ enum { FA_BWD_ATOMIC = 0, FA_BWD_DETERMINISTIC = 1 };
  *   D       : head dimension; FA_F32 and FA_BF16 support 64, 128 and 256,
  *             FA_FP8_E4M3 supports 64 and 128.
  *   causal  : 1 keeps key j only for query i >= j.
- *   scale   : factor on q.k, >= 0 and finite (usually 1/sqrt(D)).
+ *   scale   : factor on q.k, > 0 and finite (usually 1/sqrt(D)).
  * Rows are rescaled when their running max grows by more than 8 in base-2
  * units (FA_FP8_E4M3: whenever it grows), which is exact in exact arithmetic.
  */

@@ -220,6 +220,51 @@ def backward_dq_rows(q, k, v, do, causal, scale, rows, window=-1):
     return dq
 
 
+def backward_kv_rows(q, k, v, do, causal, scale, rows, window=-1):
+    """dK and dV of the listed key rows only, in float64 (for heads too long to materialise S).
+
+    Key j's gradients are column j of ``backward``'s chain rule: every query
+    row i that keeps key j contributes, through its own probabilities and dP row,
+      dS_ij = P_ij * (dP_ij - <P_i, dP_i>),  dK_j = scale sum_i dS_ij q_i,  dV_j = sum_i P_ij dO_i.
+    Each such row's P_i and <P_i, dP_i> need all of its kept keys, so the
+    scores of those rows are formed in full; only query rows that keep one of
+    the listed keys are visited (for causal masking, rows from the first
+    listed key's diagonal on). With grouped K/V heads a key's gradients are
+    sums over the query heads of its group. rows: sorted 1-D array of key
+    indices. Returns (dK, dV), each [B, Hkv, len(rows), D].
+    """
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    do = _as_f64(do)
+    B, H, N, D = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    G = _group(H, Hkv)
+    sel = np.asarray(rows, dtype=np.int64)
+    dk = np.zeros((B, Hkv, len(sel), D))
+    dv = np.zeros((B, Hkv, len(sel), v.shape[-1]))
+    if len(sel) == 0:
+        return dk, dv
+    # query rows that may keep a listed key: lo(i) <= j <= hi(i) for some listed j
+    i_all = np.arange(N)
+    lo, hi = key_bounds(i_all, N, Nk, causal, window)
+    cand = i_all[(hi >= sel.min()) & (lo <= sel.max())]
+    for b in range(B):
+        for h in range(H):
+            kh = h // G
+            for r0, r1 in _row_blocks(len(cand), Nk):
+                rr = cand[r0:r1]
+                s = scores(q[b, h, rr], k[b, kh], scale, causal, rows=rr, n_q=N, window=window)
+                p, _ = softmax_rows(s)
+                dp = do[b, h, rr] @ v[b, kh].T
+                c = (p * dp).sum(axis=1, keepdims=True)
+                ps = p[:, sel]
+                ds = ps * (dp[:, sel] - c)
+                dk[b, kh] += scale * (ds.T @ q[b, h, rr])
+                dv[b, kh] += ps.T @ do[b, h, rr]
+    return dk, dv
+
+
 def _check_cu(cu, total, B):
     cu = np.asarray(cu, dtype=np.int64)
     if cu.shape != (B + 1,) or cu[0] != 0 or cu[-1] != total or np.any(np.diff(cu) < 0):

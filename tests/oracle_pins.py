@@ -593,3 +593,38 @@ def pin_dq_rows_torch(dq_rows, tol=1e-11):
     s = s.masked_fill(j > i + (nk - nq), float("-inf"))
     (torch.softmax(s, dim=-1) @ tv * torch.from_numpy(do)).sum().backward()
     np.testing.assert_allclose(got, tq.grad.numpy()[:, :, rows], atol=tol)
+
+
+def pin_kv_rows_brute(kv_rows, brute, tol=1e-12):
+    """The row-sampled dK / dV against pure-Python loops on N <= 16 (causal, window, N_q != N_k)."""
+    for (nq, nk, causal, window, seed) in [(9, 9, False, -1, 84), (12, 7, True, -1, 85), (6, 14, True, 3, 86),
+                                           (16, 16, True, 0, 87), (7, 12, False, 2, 88)]:
+        q, do = (_rand((1, 1, nq, 5), seed + i) for i in range(2))
+        k, v = (_rand((1, 1, nk, 5), seed + 2 + i) for i in range(2))
+        rows = np.array(sorted({0, 1, nk // 2, nk - 1}))
+        gk, gv = kv_rows(q, k, v, do, causal, 0.8, rows, window=window)
+        _, bdk, bdv = brute.backward(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), do[0, 0].tolist(),
+                                     causal, 0.8, window=window)
+        np.testing.assert_allclose(gk[0, 0], np.array(bdk)[rows], atol=tol)
+        np.testing.assert_allclose(gv[0, 0], np.array(bdv)[rows], atol=tol)
+
+
+def pin_kv_rows_torch(kv_rows, tol=1e-11):
+    """The row-sampled dK / dV against torch CPU float64 autograd of the plain formula (GQA, bottom-right
+    causal): a shared K/V head's gradients are the sums over its group."""
+    import torch
+
+    B, H, Hkv, nq, nk, D = 2, 4, 2, 20, 33, 8
+    q, do = (_rand((B, H, nq, D), 94 + i) for i in range(2))
+    k, v = (_rand((B, Hkv, nk, D), 96 + i) for i in range(2))
+    rows = np.array([0, 5, 13, 14, 32])
+    gk, gv = kv_rows(q, k, v, do, True, 0.45, rows)
+    tk = torch.from_numpy(k).requires_grad_(True)
+    tv = torch.from_numpy(v).requires_grad_(True)
+    s = 0.45 * (torch.from_numpy(q) @ tk.repeat_interleave(H // Hkv, dim=1).transpose(-1, -2))
+    i = torch.arange(nq)[:, None]
+    j = torch.arange(nk)[None, :]
+    s = s.masked_fill(j > i + (nk - nq), float("-inf"))
+    (torch.softmax(s, dim=-1) @ tv.repeat_interleave(H // Hkv, dim=1) * torch.from_numpy(do)).sum().backward()
+    np.testing.assert_allclose(gk, tk.grad.numpy()[:, :, rows], atol=tol)
+    np.testing.assert_allclose(gv, tv.grad.numpy()[:, :, rows], atol=tol)

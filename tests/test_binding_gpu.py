@@ -39,6 +39,11 @@ def test_fp8_forward_outputs_checked():
         fa.fwd_fp8(q, q, q, out=_t(1, 1, 32, 64))
     with pytest.raises(ValueError):
         fa.fwd_fp8(q, q, q, q_descale=torch.ones(1, dtype=torch.float64, device=DEV))
+    # bf16 (or any non-e4m3) tensors would be read as codes: refused
+    for dt in (BF, torch.float32, torch.int8):
+        x = _t(1, 1, 64, 64, dtype=dt)
+        with pytest.raises(ValueError):
+            fa.fwd_fp8(x, x, x)
 
 
 def test_backward_outputs_and_workspace_checked():

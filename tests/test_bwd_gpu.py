@@ -52,7 +52,7 @@ def test_bwd_causal_workload_full(variant):
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_small_shapes(variant, D, causal):
-    for i, N in enumerate([1, 2, 17, 63, 65, 129, 300]):
+    for i, N in enumerate([1, 2, 17, 28, 29, 30, 31, 63, 65, 129, 300]):
         dev, ref = prepare("bf16", (1, 2, N, D), 2000 + 31 * i + D, with_grad=True)
         scale = 1.0 / math.sqrt(D)
         g = _grads(dev, causal, scale, VARIANTS[variant])

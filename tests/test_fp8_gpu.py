@@ -1,11 +1,12 @@
 """GPU parity of the FP8 path: per-tensor quantisation (bit-exact) and the e4m3 forward (6e-2)."""
+import concurrent.futures as cf
 import math
 
 import numpy as np
 import pytest
 import torch
 
-from gpu_util import DEV, REL_FP8, TOL_FP8, f32_tensor, max_abs, rel_fro, sample_rows, to_f64
+from gpu_util import DEV, REL_FP8, TOL_FP8, f32_tensor, max_abs, sample_rows, to_f64
 from oracle import attention, codecs
 from tiled_online_softmax_amd import fa, inputs
 
@@ -32,11 +33,12 @@ def test_quantize_zero_tensor():
     assert desc_gpu.item() == 1.0 and int(codes_gpu.cpu().max()) == 0
 
 
-def _fp8_case(shape, causal, seed, rows=None, heads=None):
+def _fp8_case(shape, causal, seed, rows=None):
     """Quantise seeded N(0,1) draws on the GPU, run the FP8 forward, compare with the oracle.
 
     The oracle quantises the same float32 draws with its own codec and runs on the
-    dequantised values; the codes are also compared bit-exactly (on the checked heads).
+    dequantised values; the codes are also compared bit-exactly. Heads are independent,
+    so the oracle's work is spread over host threads one head at a time.
     """
     q, k, v = inputs.draw(shape, seed, 3)
     dev = [fa.quantize_fp8(f32_tensor(x)) for x in (q, k, v)]
@@ -45,37 +47,48 @@ def _fp8_case(shape, causal, seed, rows=None, heads=None):
     o, lse = fa.fwd_fp8(dev[0][0], dev[1][0], dev[2][0], causal=causal, scale=scale,
                         q_descale=dev[0][1], k_descale=dev[1][1], v_descale=dev[2][1])
     torch.cuda.synchronize()
-    heads = list(range(shape[1])) if heads is None else heads
-    ref_in = []
-    for x, (codes_gpu, desc_gpu) in zip((q, k, v), dev):
+    descales = []
+    for x, (_, desc_gpu) in zip((q, k, v), dev):
         amax = np.float32(np.max(np.abs(x)))
         assert desc_gpu.item() == float(np.float32(amax / np.float32(448)))
-        xs = (x[:, heads] * (np.float32(448) / amax)).astype(np.float32)
-        codes_ref = codecs.f64_to_e4m3(xs.astype(np.float64))
-        np.testing.assert_array_equal(codes_gpu[:, heads].cpu().numpy(), codes_ref)
-        ref_in.append(codecs.dequantize(codes_ref, desc_gpu.item()))
-    o_ref, lse_ref = attention.forward(*ref_in, causal, scale, rows=rows)
-    o_gpu, lse_gpu = to_f64(o)[:, heads], to_f64(lse)[:, heads]
-    if rows is not None:
-        o_gpu, lse_gpu = o_gpu[:, :, rows], lse_gpu[:, :, rows]
-    eo, el = max_abs(o_gpu, o_ref), max_abs(lse_gpu, lse_ref)
-    print(f"[fp8 {shape} causal={causal}] max|dO|={eo:.3e} max|dlse|={el:.3e} relO={rel_fro(o_gpu, o_ref):.3e}",
-          flush=True)
+        descales.append((np.float32(448) / amax, desc_gpu.item()))
+    codes_gpu = [c.cpu().numpy() for c, _ in dev]
+    o_all, lse_all = to_f64(o), to_f64(lse)
+
+    def head(h):
+        ref_in = []
+        for x, (mul, desc), cg in zip((q, k, v), descales, codes_gpu):
+            xs = (x[:, h:h + 1] * mul).astype(np.float32)
+            codes_ref = codecs.f64_to_e4m3(xs.astype(np.float64))
+            np.testing.assert_array_equal(cg[:, h:h + 1], codes_ref)
+            ref_in.append(codecs.dequantize(codes_ref, desc))
+        o_ref, lse_ref = attention.forward(*ref_in, causal, scale, rows=rows)
+        o_g, lse_g = o_all[:, h:h + 1], lse_all[:, h:h + 1]
+        if rows is not None:
+            o_g, lse_g = o_g[:, :, rows], lse_g[:, :, rows]
+        return max_abs(o_g, o_ref), max_abs(lse_g, lse_ref), float(np.sum((o_g - o_ref) ** 2)), \
+            float(np.sum(o_ref ** 2))
+
+    with cf.ThreadPoolExecutor(max_workers=min(16, shape[1])) as ex:
+        res = list(ex.map(head, range(shape[1])))
+    eo, el = max(r[0] for r in res), max(r[1] for r in res)
+    rel = math.sqrt(sum(r[2] for r in res) / sum(r[3] for r in res))
+    print(f"[fp8 {shape} causal={causal}] max|dO|={eo:.3e} max|dlse|={el:.3e} relO={rel:.3e}", flush=True)
     assert eo <= TOL_FP8 and el <= TOL_FP8
-    assert rel_fro(o_gpu, o_ref) <= REL_FP8
+    assert rel <= REL_FP8
 
 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp8_small(D, causal):
-    for i, N in enumerate([1, 5, 64, 65, 200, 1000]):
+    for i, N in enumerate([1, 5, 28, 29, 30, 31, 64, 65, 200, 1000]):
         _fp8_case((1, 2, N, D), causal, 300 + i + D)
 
 
 def test_fp8_long_context_workload_sampled():
-    """B=1 H=32 N=32768 D=128 e4m3 causal: sampled rows of 4 of the 32 heads (plus bit-exact codes)."""
+    """B=1 H=32 N=32768 D=128 e4m3 causal: sampled rows of every head (plus bit-exact codes)."""
     w = inputs.WORKLOADS["long_fp8_causal"]
-    _fp8_case(w.shape, w.causal, w.seed, rows=sample_rows(w.N), heads=[0, 9, 22, 31])
+    _fp8_case(w.shape, w.causal, w.seed, rows=sample_rows(w.N))
 
 
 def test_fp8_unit_descales_via_fa_fwd():

@@ -42,7 +42,8 @@ def test_single_head_f32_workload():
     _check("f32", o, lse, o_ref, lse_ref, w.name)
 
 
-SMALL_N = [1, 2, 3, 15, 16, 17, 31, 63, 65, 127, 129, 300]
+# 28..31: rows ending just short of a 32-row wave block (a stale-accumulator bug once hid there)
+SMALL_N = [1, 2, 3, 15, 16, 17, 28, 29, 30, 31, 63, 65, 127, 129, 300]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -79,16 +80,66 @@ def test_d256_bf16_workload_sampled():
     assert abs(float(np.mean(lse)) - math.log(w.N)) < 0.1
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("tau", [0.0, 3.0, 8.0, 30.0])
-def test_rescale_threshold_variants(tau):
-    """Conditional rescaling is exact for every threshold: all agree with the oracle."""
-    for dtype in ("f32", "bf16"):
-        # Inputs x2.5 give scores with a 6x larger spread (|s| up to ~25), so running maxima
-        # grow across tiles. The bounds scale with the magnitudes: float32 rounding of scores
-        # near 25 is ~25 * 2^-24 per operation (4e-5 instead of 1e-5), and O = P V is 2.5x
-        # larger, so its bf16 rounding bound is 2.5 x 2e-2.
-        o, lse, o_ref, lse_ref = _run(dtype, (1, 2, 700, 64), True, 5, multiplier=2.5, rescale=tau)
-        _check(dtype, o, lse, o_ref, lse_ref, f"{dtype} tau={tau}", f32_tol=4e-5, bf16_o_tol=2.5 * TOL_BF16_O)
+def test_rescale_threshold_variants(tau, D, dtype):
+    """Conditional rescaling is exact for every threshold: on N(0,1) inputs all thresholds meet the
+    stated tolerances. Causal N = 700 spans 11 (64-key) or 22 (32-key) key tiles, so the running max
+    of a row grows across tiles and tau = 0 and 3 rescale non-zero accumulators. bf16 D = 128 runs
+    the phase-alternating kernel, D = 64 and 256 the software-pipelined one."""
+    o, lse, o_ref, lse_ref = _run(dtype, (1, 2, 700, D), True, 5 + D, rescale=tau)
+    _check(dtype, o, lse, o_ref, lse_ref, f"{dtype} D{D} tau={tau}")
+
+
+# Planted keys: rows 600, 601, 650 and 1100 of K set to 6 in every coordinate. Their score for
+# query i is 6 * sum_d q_id / sqrt(D) = 6 z_i with z_i ~ N(0, 1), so for about a tenth of the
+# rows the score jumps far above everything seen in the first nine 64-key tiles.
+PLANTED = (600, 601, 650, 1100)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_rescale_on_planted_keys_default_threshold(dtype, D):
+    """At the default threshold (8 in log2 units) the reference max moves, and the accumulator is
+    rescaled, only when a later tile beats it by a factor 256; planted keys in late tiles force that
+    on many rows of every wave. Checked at the stated tolerances."""
+    N = 1200
+    scale = 1.0 / math.sqrt(D)
+    dev, ref = prepare(dtype, (1, 2, N, D), 6100 + D)
+    for j in PLANTED:
+        dev["k"][:, :, j] = 6.0
+        ref["k"][:, :, j] = 6.0
+    # rows whose planted score exceeds every score of the keys before the first planted one by more
+    # than 8 log2 units: the reference max never exceeds those scores, so these rows must rescale
+    j0 = PLANTED[0]
+    s_before = np.einsum("bhid,bhjd->bhij", ref["q"], ref["k"][:, :, :j0]) * scale
+    before_max = np.where(np.arange(j0)[None, :] <= np.arange(N)[:, None], s_before, -np.inf).max(axis=-1)
+    planted = 6.0 * ref["q"].sum(axis=-1) * scale
+    jumps = (planted - before_max) * math.log2(math.e) > 8.0
+    jumps[:, :, :j0] = False  # rows before the first planted key never see one
+    assert jumps.sum() >= 50, int(jumps.sum())
+    o, lse = fa.fwd(dev["q"], dev["k"], dev["v"], causal=True, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = attention.forward(ref["q"], ref["k"], ref["v"], True, scale)
+    tag = f"{dtype} D{D} planted ({int(jumps.sum())} rows jump)"
+    if dtype == "bf16":
+        _check(dtype, to_f64(o), to_f64(lse), o_ref, lse_ref, tag)
+        return
+    # float32: O at the stated 1e-5. The stated 1e-5 on lse is for N(0,1) inputs, whose scores stay
+    # below about 5; planted rows reach |s| ~ 14. A float32 score summed over D products carries a
+    # rounding error of about sqrt(D) u |s| (u = 2^-24), and lse = max + ln(sum) inherits it from the
+    # row's dominant scores, so a row's lse is held to max(1e-5, 4 sqrt(D) u max_j |s_ij|).
+    s_all = np.einsum("bhid,bhjd->bhij", ref["q"], ref["k"]) * scale
+    s_abs = np.where(np.arange(N)[None, :] <= np.arange(N)[:, None], np.abs(s_all), 0.0).max(axis=-1)
+    tol_lse = np.maximum(TOL_F32, 4.0 * math.sqrt(D) * 2.0 ** -24 * s_abs)
+    o_g, lse_g = to_f64(o), to_f64(lse)
+    eo = max_abs(o_g, o_ref)
+    dl = np.abs(lse_g - lse_ref)
+    print(f"[{tag}] max|dO|={eo:.3e} max|dlse|={dl.max():.3e} max(|dlse|/tol)={(dl / tol_lse).max():.3f}",
+          flush=True)
+    assert eo <= TOL_F32, (tag, eo)
+    assert (dl <= tol_lse).all(), (tag, float((dl / tol_lse).max()))
 
 
 def test_zero_query_closed_form():

@@ -1,8 +1,9 @@
 """The longest heads of the parity suite: a 262,144-row causal forward and a 65,536-row backward.
 
 Long heads exercise the tile ranges, 32-bit in-head offsets and launch orders at their largest. The oracle
-computes the sampled query rows exactly (rows are independent); for the backward, dQ rows are exact and
-dV is checked through an identity that holds at any size.
+computes the sampled query rows exactly (rows are independent); for the backward, dQ rows and the dK / dV
+rows of sampled keys in the last 4096 of the head are exact (a key's gradients need only the query rows
+that keep it), and dV is also checked through an identity that holds at any size.
 """
 import math
 
@@ -40,6 +41,16 @@ def test_long_causal_forward_sampled():
     assert eo <= TOL_BF16_O and el <= TOL_BF16_LSE and rel <= 1e-2
 
 
+def _key_rows(N, span=4096):
+    """Keys of the last `span` rows: a suffix, the edges of 32-, 64-, 128- and 256-key tiles, and a stride."""
+    lo = N - span
+    r = set(range(N - 96, N)) | set(range(lo, lo + 32)) | set(range(lo, N, 997))
+    for t in (32, 64, 128, 256):
+        for e in (lo + t, lo + span // 2 - (span // 2) % t, N - t):
+            r |= {e - 1, e}
+    return np.array(sorted(x for x in r if lo <= x < N), dtype=np.int64)
+
+
 def test_long_causal_backward_dq_rows_and_dv_sum():
     B, H, N, D = 1, 2, 65536, 128
     scale = 1.0 / math.sqrt(D)
@@ -55,6 +66,13 @@ def test_long_causal_backward_dq_rows_and_dv_sum():
     e, rel = max_abs(dq_g, dq_ref), rel_fro(dq_g, dq_ref)
     print(f"[long bwd] {len(rows)} dQ rows: max|d|={e:.3e} rel={rel:.3e}", flush=True)
     assert e <= TOL_BF16_GRAD and rel <= 2e-2
+    krows = _key_rows(N)
+    dk_ref, dv_ref = attention.backward_kv_rows(ref["q"], ref["k"], ref["v"], ref["do"], True, scale, krows)
+    dk_g, dv_g = to_f64(dk)[:, :, krows], to_f64(dv)[:, :, krows]
+    ek, ev = max_abs(dk_g, dk_ref), max_abs(dv_g, dv_ref)
+    rk, rv = rel_fro(dk_g, dk_ref), rel_fro(dv_g, dv_ref)
+    print(f"[long bwd] {len(krows)} dK/dV rows: max|d| dK={ek:.3e} dV={ev:.3e} rel {rk:.3e} {rv:.3e}", flush=True)
+    assert ek <= TOL_BF16_GRAD and ev <= TOL_BF16_GRAD and rk <= 2e-2 and rv <= 2e-2
     # Rows of P sum to one, so sum_j dV_j = sum_j sum_i P_ij dO_i = sum_i dO_i exactly. The GPU's dV
     # entries are bf16-rounded (relative 2^-9 each), so their sum is allowed 8 * 2^-9 * ||dV column||.
     dv64, dk64 = to_f64(dv), to_f64(dk)

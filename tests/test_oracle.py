@@ -122,3 +122,11 @@ def test_dq_rows_brute():
 
 def test_dq_rows_torch():
     pins.pin_dq_rows_torch(attention.backward_dq_rows)
+
+
+def test_kv_rows_brute():
+    pins.pin_kv_rows_brute(attention.backward_kv_rows, brute)
+
+
+def test_kv_rows_torch():
+    pins.pin_kv_rows_torch(attention.backward_kv_rows)

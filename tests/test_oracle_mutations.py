@@ -447,3 +447,56 @@ def test_unmutated_dq_rows_factory_passes():
     f = _dq_rows_factory()
     pins.pin_dq_rows_brute(f, brute)
     pins.pin_dq_rows_torch(f)
+
+
+def _kv_rows_factory(mutant=None):
+    """Copies of the row-sampled dK / dV with one planted mistake each."""
+
+    def kv_rows(q, k, v, do, causal, scale, rows, window=-1):
+        q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+        B, H, N, D = q.shape
+        G = H // k.shape[1]
+        rows = np.asarray(rows)
+        cols = np.minimum(rows + 1, k.shape[2] - 1) if mutant == "row_shift" else rows
+        dk = np.zeros((B, k.shape[1], len(rows), D))
+        dv = np.zeros_like(dk)
+        # the "late_queries" mutant visits only query rows from the last listed key on
+        first = int(rows.max()) - (k.shape[2] - N) if mutant == "late_queries" else 0
+        qr = np.arange(max(0, first), N)
+        for b in range(B):
+            for h in range(H):
+                kk, vv = k[b, h // G], v[b, h // G]
+                s = attention.scores(q[b, h, qr], kk, scale, causal, rows=qr, n_q=N, window=window)
+                p, _ = attention.softmax_rows(s)
+                dp = do[b, h, qr] @ vv.T
+                c = 0.0 if mutant == "no_jacobian" else (p * dp).sum(axis=1, keepdims=True)
+                ds = p[:, cols] * (dp[:, cols] - c)
+                sc = 1.0 if mutant == "no_scale" else scale
+                kh = h // G
+                if mutant == "overwrite" and h % G:
+                    dk[b, kh] = 0.0
+                    dv[b, kh] = 0.0
+                dk[b, kh] += sc * (ds.T @ q[b, h, qr])
+                dv[b, kh] += (dp[:, cols] if mutant == "dp_for_p" else p[:, cols]).T @ do[b, h, qr]
+        return dk, dv
+
+    return kv_rows
+
+
+@pytest.mark.parametrize("mutant", ["row_shift", "late_queries", "no_jacobian", "no_scale", "overwrite",
+                                    "dp_for_p"])
+def test_kv_rows_mutants_fail_a_pin(mutant):
+    f = _kv_rows_factory(mutant)
+    failures = 0
+    for pin in (lambda: pins.pin_kv_rows_brute(f, brute), lambda: pins.pin_kv_rows_torch(f)):
+        try:
+            pin()
+        except AssertionError:
+            failures += 1
+    assert failures > 0, mutant
+
+
+def test_unmutated_kv_rows_factory_passes():
+    f = _kv_rows_factory()
+    pins.pin_kv_rows_brute(f, brute)
+    pins.pin_kv_rows_torch(f)

@@ -253,6 +253,8 @@ def fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
             lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """FP8 (e4m3 codes, uint8 or float8_e4m3fn tensors) forward with per-tensor descales (1-element device tensors)."""
     _check_qkv(q, k, v)
+    if q.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise ValueError("fwd_fp8 takes e4m3 codes (uint8 or float8_e4m3fn tensors)")
     B, H, N, D = q.shape
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if out is None:
