@@ -60,6 +60,19 @@ def max_abs(a: np.ndarray, b: np.ndarray) -> float:
     return float(np.max(np.abs(a - b))) if a.size else 0.0
 
 
+# One bf16 rounding unit: a value stored as bf16 is off by at most half an ulp, which is at most
+# 2^-8 of its magnitude (at the bottom of a binade). No bf16 output can meet a fixed max-abs bound
+# below 2^-8 max|g|, and the backward's gradients reach |g| ~ 5 (2^-8 * 5 = 0.02).
+BF16_ULP_REL = 2.0 ** -8
+
+
+def grad_err(a: np.ndarray, ref: np.ndarray) -> float:
+    """Backward error measure: max over elements of |a - ref| - 2^-8 |ref|, i.e. the error beyond one
+    bf16 rounding unit of the exact gradient; compared with the max-abs gradient tolerance."""
+    assert np.isfinite(a).all(), "non-finite GPU output"
+    return float(np.max(np.abs(a - ref) - BF16_ULP_REL * np.abs(ref))) if a.size else 0.0
+
+
 def rel_fro(a: np.ndarray, b: np.ndarray) -> float:
     den = float(np.linalg.norm(b))
     return float(np.linalg.norm(a - b)) / den if den > 0 else float(np.linalg.norm(a))

@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import (DEV, TOL_BF16_GRAD, TOL_BF16_LSE, TOL_BF16_O, TOL_F32, max_abs, prepare, rel_fro,
+from gpu_util import (DEV, TOL_BF16_GRAD, grad_err, TOL_BF16_LSE, TOL_BF16_O, TOL_F32, max_abs, prepare, rel_fro,
                       to_f64)
 from oracle import attention
 from tiled_online_softmax_amd import fa
@@ -109,7 +109,7 @@ def test_strided_bwd(variant, case):
         assert all(_same(a, b) for a, b in zip(g, g_c)), "strided backward differs from the contiguous one"
     g_ref = attention.backward(ref["q"], ref["k"], ref["v"], ref["do"], causal, 1 / math.sqrt(D),
                                window=_win(window))
-    errs = [max_abs(to_f64(a), b) for a, b in zip(g, g_ref)]
+    errs = [grad_err(to_f64(a), b) for a, b in zip(g, g_ref)]
     tol = [TOL_BF16_GRAD, TOL_BF16_GRAD * math.sqrt(H // Hkv), TOL_BF16_GRAD * math.sqrt(H // Hkv)]
     print(f"[strided bwd {variant} {case}] dQ {errs[0]:.3e} dK {errs[1]:.3e} dV {errs[2]:.3e}", flush=True)
     assert all(e <= t for e, t in zip(errs, tol))
@@ -168,7 +168,7 @@ def test_varlen_bwd(variant, causal, window):
     torch.cuda.synchronize()
     g_ref = attention.backward_varlen(ref["q"], ref["k"], ref["v"], ref["do"], cu_q, cu_k, causal,
                                       1 / math.sqrt(D), window=_win(window))
-    errs = [max_abs(to_f64(a), b) for a, b in zip(g, g_ref)]
+    errs = [grad_err(to_f64(a), b) for a, b in zip(g, g_ref)]
     rels = [rel_fro(to_f64(a), b) for a, b in zip(g, g_ref)]
     print(f"[varlen bwd {variant} causal={causal} w={window}] dQ {errs[0]:.3e} dK {errs[1]:.3e} "
           f"dV {errs[2]:.3e} rel {max(rels):.3e}", flush=True)
@@ -198,7 +198,7 @@ def test_rows_without_keys(D):
         g = fa.bwd(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, causal=True, variant=variant)
         torch.cuda.synchronize()
         assert not g[0][:, :, :e].any()
-        errs = [max_abs(to_f64(a), b) for a, b in zip(g, g_ref)]
+        errs = [grad_err(to_f64(a), b) for a, b in zip(g, g_ref)]
         assert errs[0] <= TOL_BF16_GRAD and max(errs[1:]) <= TOL_BF16_GRAD * math.sqrt(2), errs
     # the f32 forward and a query tile whose rows all keep no key
     dev32, ref32 = prepare("f32", (1, 2, 200, 64), 6510, nk=40)
@@ -238,4 +238,4 @@ def test_workload_varlen_bf16():
         t = lambda x: x[s].transpose(1, 0, 2)[None]
         g_ref = attention.backward(t(ref["q"]), t(ref["k"]), t(ref["v"]), t(ref["do"]), True, w.scale)
         for a, r in zip(g, g_ref):
-            assert max_abs(to_f64(a)[s].transpose(1, 0, 2)[None], r) <= TOL_BF16_GRAD
+            assert grad_err(to_f64(a)[s].transpose(1, 0, 2)[None], r) <= TOL_BF16_GRAD

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import (REL_BF16, TOL_BF16_GRAD, TOL_BF16_LSE, TOL_BF16_O, TOL_F32, max_abs, prepare, rel_fro,
+from gpu_util import (REL_BF16, grad_err, TOL_BF16_GRAD, TOL_BF16_LSE, TOL_BF16_O, TOL_F32, max_abs, prepare, rel_fro,
                       sample_rows, to_f64)
 from oracle import attention
 from tiled_online_softmax_amd import fa, inputs
@@ -65,10 +65,10 @@ def test_full_window_equals_no_window():
 
 
 def _check_grads(g, g_ref, tag, group=1):
-    errs = [max_abs(a, b) for a, b in zip(g, g_ref)]
+    errs = [grad_err(a, b) for a, b in zip(g, g_ref)]
     rels = [rel_fro(a, b) for a, b in zip(g, g_ref)]
     tols = [TOL_BF16_GRAD, TOL_BF16_GRAD * math.sqrt(group), TOL_BF16_GRAD * math.sqrt(group)]
-    print(f"[{tag}] max|d| dQ={errs[0]:.3e} dK={errs[1]:.3e} dV={errs[2]:.3e} rel={max(rels):.3e}", flush=True)
+    print(f"[{tag}] max(|d|-ulp) dQ={errs[0]:.3e} dK={errs[1]:.3e} dV={errs[2]:.3e} rel={max(rels):.3e}", flush=True)
     assert all(e <= t for e, t in zip(errs, tols)), (tag, errs, tols)
     if g[0].shape[2] >= 64:
         assert max(rels) <= 2e-2, (tag, rels)

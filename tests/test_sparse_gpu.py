@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import (DEV, TOL_BF16_GRAD, TOL_BF16_LSE, TOL_BF16_O, TOL_F32, max_abs, prepare, rel_fro,
+from gpu_util import (DEV, TOL_BF16_GRAD, grad_err, TOL_BF16_LSE, TOL_BF16_O, TOL_F32, max_abs, prepare, rel_fro,
                       to_f64)
 from oracle import attention
 from tiled_online_softmax_amd import fa
@@ -127,7 +127,7 @@ def test_sparse_bwd(variant, case):
     torch.cuda.synchronize()
     g_ref = attention.backward(ref["q"], ref["k"], ref["v"], ref["do"], causal, 1 / math.sqrt(D),
                                window=_win(window), block_mask=m)
-    errs = [max_abs(to_f64(a), b) for a, b in zip(g, g_ref)]
+    errs = [grad_err(to_f64(a), b) for a, b in zip(g, g_ref)]
     rels = [rel_fro(to_f64(a), b) for a, b in zip(g, g_ref)]
     print(f"[sparse bwd {variant} {case}] dQ {errs[0]:.3e} dK {errs[1]:.3e} dV {errs[2]:.3e} rel {max(rels):.3e}",
           flush=True)
@@ -201,6 +201,6 @@ def test_workload_sparse_bf16():
         assert eo <= TOL_BF16_O and el <= TOL_BF16_LSE
     sl = (slice(1, 2), slice(7, 8))
     g_ref = attention.backward(ref["q"][sl], ref["k"][sl], ref["v"][sl], ref["do"][sl], True, w.scale, block_mask=m)
-    errs = [max_abs(to_f64(a)[sl], r) for a, r in zip(g, g_ref)]
+    errs = [grad_err(to_f64(a)[sl], r) for a, r in zip(g, g_ref)]
     print(f"[sparse workload bwd] dQ {errs[0]:.3e} dK {errs[1]:.3e} dV {errs[2]:.3e}", flush=True)
     assert max(errs) <= TOL_BF16_GRAD
