@@ -378,6 +378,26 @@ int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* o,
                 int B, int H, int N, int D, int causal, float scale, int dtype,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): fa_bwd with
+ * its workspace taken from a static device array of FA_NOALLOC_SCRATCH_BYTES
+ * that the library holds on every GPU it runs on, from load until the process
+ * ends. Nothing is allocated or freed. Arguments, variants, results and
+ * errors as for fa_bwd; a problem whose fa_bwd_workspace_size exceeds
+ * FA_NOALLOC_SCRATCH_BYTES is refused with FA_ERR_WORKSPACE before any HIP
+ * call. Every call on a GPU uses that GPU's one array, which keeps the last
+ * call's contents (the kernels initialise what they read): calls that overlap
+ * on one GPU (other streams, other threads) race and must be serialised by the
+ * caller. The first call on a device looks the array up (hipGetSymbolAddress);
+ * a failure there returns FA_ERR_HIP.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                   const void* dO, const float* lse, void* dq, void* dk,
+                   void* dv, int B, int H, int N, int D, int causal,
+                   float scale, int dtype, int variant, void* stream);
+
 /* Static text for a status code. */
 const char* fa_status_string(int status);
 

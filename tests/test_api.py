@@ -351,3 +351,26 @@ def test_block_sparse_validation():
     assert bwd(variant=2) == fa.FA_ERR_INVALID_ARG
     assert bwd(qi=None) == fa.FA_ERR_INVALID_ARG
     assert bwd(wsb=ws - 1) == fa.FA_ERR_WORKSPACE
+
+
+def _bwd_noalloc(**kw):
+    a = dict(B=1, H=1, N=16, D=64, causal=0, scale=0.125, dtype=fa.FA_BF16, variant=fa.FA_BWD_DETERMINISTIC)
+    a.update(kw)
+    return fa.lib().fa_bwd_noalloc(P, P, P, P, P, P, P, P, P, a["B"], a["H"], a["N"], a["D"], a["causal"],
+                                   a["scale"], a["dtype"], a["variant"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(N=0), fa.FA_ERR_INVALID_ARG, ">= 1"),
+    (dict(scale=-1.0), fa.FA_ERR_INVALID_ARG, "scale"),
+    (dict(variant=5), fa.FA_ERR_INVALID_ARG, "variant"),
+    (dict(dtype=fa.FA_F32), fa.FA_ERR_UNSUPPORTED, "FA_BF16"),
+    (dict(D=96), fa.FA_ERR_UNSUPPORTED, "D=96"),
+    # atomic variant at B4 H16 N2048 D128: 1 MiB of row statistics + 64 MiB of dQ accumulator > 64 MiB
+    (dict(B=4, H=16, N=2048, D=128, variant=fa.FA_BWD_ATOMIC), fa.FA_ERR_WORKSPACE, "static scratch"),
+    (dict(B=64, H=64, N=4096, D=64), fa.FA_ERR_WORKSPACE, "static scratch"),
+])
+def test_bwd_noalloc_validation(kw, status, msg):
+    """fa_bwd_noalloc validates like fa_bwd and refuses problems beyond its static scratch, before any HIP call."""
+    assert _bwd_noalloc(**kw) == status
+    assert msg in fa.last_error()

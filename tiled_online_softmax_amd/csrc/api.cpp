@@ -203,6 +203,14 @@ Layout strides_from(const long long* st, int n_tensors) {
 
 }  // namespace
 
+int fa::api_fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
 extern "C" {
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int D, int causal,

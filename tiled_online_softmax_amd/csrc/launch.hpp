@@ -242,4 +242,7 @@ hipError_t block_lists_launch(const BlockListParams& p, int B, hipStream_t st);
 
 hipError_t quantize_fp8_launch(const float* x, size_t n, void* codes, float* descale, hipStream_t st);
 
+// Sets the calling thread's error message (fa_last_error) and returns `status`.
+int api_fail(int status, const char* fmt, ...);
+
 }  // namespace fa

@@ -25,7 +25,7 @@ FA_BWD_ATOMIC, FA_BWD_DETERMINISTIC = 0, 1
 EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_general", "fa_fwd_strided", "fa_fwd_varlen", "fa_block_lists",
             "fa_fwd_sparse", "fa_fwd_ex", "fa_fwd_fp8", "fa_quantize_fp8", "fa_bwd_workspace_size", "fa_bwd",
             "fa_bwd_gqa", "fa_bwd_general", "fa_bwd_strided", "fa_bwd_sparse", "fa_bwd_varlen", "fa_bwd_dkdv",
-            "fa_status_string", "fa_last_error")
+            "fa_bwd_noalloc", "fa_status_string", "fa_last_error")
 BLOCK = 128  # rows and columns of a block of a block-sparse mask
 
 
@@ -65,13 +65,15 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd_varlen.argtypes = [_vp] * 11 + [_i] * 10 + [_f, _i, _i, _vp, _sz, _vp]
         L.fa_bwd_sparse.argtypes = [_vp] * 9 + [_i] * 8 + [_f, _i, _i] + [_vp] * 4 + [_vp, _sz, _vp]
         L.fa_bwd_dkdv.argtypes = [_vp] * 8 + [_i] * 5 + [_f, _i, _vp, _sz, _vp]
+        L.fa_bwd_noalloc.argtypes = [_vp] * 9 + [_i] * 5 + [_f, _i, _i, _vp]
         L.fa_status_string.argtypes = [_i]
         L.fa_status_string.restype = ctypes.c_char_p
         L.fa_last_error.argtypes = []
         L.fa_last_error.restype = ctypes.c_char_p
         for name in ("fa_fwd", "fa_fwd_gqa", "fa_fwd_general", "fa_fwd_strided", "fa_fwd_varlen", "fa_block_lists",
                      "fa_fwd_sparse", "fa_fwd_ex", "fa_fwd_fp8", "fa_quantize_fp8", "fa_bwd", "fa_bwd_gqa",
-                     "fa_bwd_general", "fa_bwd_strided", "fa_bwd_sparse", "fa_bwd_varlen", "fa_bwd_dkdv"):
+                     "fa_bwd_general", "fa_bwd_strided", "fa_bwd_sparse", "fa_bwd_varlen", "fa_bwd_dkdv",
+                     "fa_bwd_noalloc"):
             getattr(L, name).restype = _i
         _lib = L
     return _lib
@@ -346,6 +348,27 @@ def bwd(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None
     _check(lib().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
                         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, D, int(causal), scale, _dtype_code(q),
                         variant, workspace.data_ptr(), workspace.numel(), _stream(q)))
+    return dq, dk, dv
+
+
+@_on_device
+def bwd_noalloc(q, k, v, o, do, lse, causal: bool = False, scale: Optional[float] = None,
+                variant: int = FA_BWD_DETERMINISTIC, dq=None, dk=None, dv=None):
+    """Attention backward (bf16, contiguous [B, H, N, D]) through fa_bwd_noalloc: the library takes its
+    workspace from a static device array (FA_NOALLOC_SCRATCH_BYTES), so the C call allocates nothing.
+    Outputs the caller does not pass are allocated here by torch. Returns (dQ, dK, dV)."""
+    _check_qkv(q, k, v, o, do)
+    B, H, N, D = q.shape
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check_like(lse, (B, H, N), torch.float32, q.device, "lse")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check_like(t, q.shape, q.dtype, q.device, name)
+    _check(lib().fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, D, int(causal),
+                                scale, _dtype_code(q), variant, _stream(q)))
     return dq, dk, dv
 
 
