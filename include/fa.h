@@ -238,9 +238,13 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
  *              fa_quantize_fp8 on the same stream without a host sync).
  *   o        : [B, H, N, D] bfloat16; lse: [B, H, N] float.
  *   D        : 64 or 128.
- * Scores use fp8 MFMA with the descales folded into the score scale; the
- * probabilities are encoded as e4m3(p * 448) for the P.V product while the
- * row sums and lse use the unencoded float32 p.
+ * Both products use fp8 MFMA, with the descales folded into the score scale
+ * and the output. The probabilities are encoded as e4m3(p * 448) for the P.V
+ * product while the row sums and lse use the unencoded float32 p. On key
+ * tiles that need masking (the causal diagonal, a ragged tail) -- which hold
+ * every key of the shortest rows -- a second e4m3 term carries the rounding
+ * residual of the first, so those products see about 2^-8 relative error in
+ * P instead of up to 2^-4.
  */
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int N, int D, int causal, float scale,

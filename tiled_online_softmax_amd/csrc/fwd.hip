@@ -24,16 +24,33 @@
 
 namespace fa {
 
+// A compile-time flag passed as a value (to instantiate a lambda per case).
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+
 // ---------------------------------------------------------------------------
-// Forward with direct global->LDS tile loads (float32, bf16 and e4m3).
+// Forward with direct global->LDS tile loads (float32 and e4m3 inputs; bf16
+// inputs take the kernels further down).
 //
 // K and V tiles are copied row-major into swizzled LDS tiles by LDS-DMA
 // buffer loads (no register staging, no LDS store instructions). S^T = K Q^T
-// reads K rows as MFMA A operands; the P.V product reads V^T operands with
-// transposing LDS reads (ds_read_b64_tr_b16 for bf16, ds_read_b64_tr_b8 for
-// e4m3), so V needs no transposed copy. float32 reads V rows directly (its
-// 32x32x2 MFMA contracts two keys held by the two lane halves). The tile loop is unrolled by two so the stage base of
-// every LDS read is an immediate.
+// reads K rows as MFMA A operands.
+//   * float32: the 32x32x2 MFMA contracts two keys held by the two lane
+//     halves, so P.V reads V rows directly.
+//   * e4m3: both products run on the 32x32x64 fp8 MFMA. The descales fold
+//     into the score scale and the output; V^T operands are read with
+//     transposing 8-bit LDS reads (ds_read_b64_tr_b8); P is encoded as
+//     e4m3(p * 448), the exponentials taking log2 448 into their offset. e4m3
+//     keeps 3 significand bits, so an encoded probability is off by up to 2^-4
+//     of itself, and a row whose keys all sit in one or two tiles would carry
+//     that into O almost undiluted. On tiles that need masking (the causal
+//     diagonal, the ragged tail, a window start: all the keys of such short
+//     rows) P is therefore encoded as two e4m3 terms, the rounding and its
+//     residual, which multiply the same V^T operand: about 2^-8 relative error.
+// The tile loop is unrolled by two so the stage base of every LDS read is an
+// immediate.
 // ---------------------------------------------------------------------------
 // log2(448): e4m3's largest finite value is 448; P is encoded as e4m3(p * 448).
 constexpr float kLog2P8 = 8.80735492205760410744f;
@@ -63,6 +80,8 @@ template <class C, bool SAME, bool SPARSE>
 __global__ void __launch_bounds__(C::NT)
 __attribute__((amdgpu_waves_per_eu(C::OCC, C::OCC)))
 fwd_kernel(FwdParams P) {
+  static_assert(C::elt != Elt::BF16, "bf16 inputs take fwd_pipe_kernel / fwd_pp_kernel");
+  constexpr bool FP8 = C::elt == Elt::FP8;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
   constexpr int D = C::D, BN = C::BN, NB = C::NB, NE = C::NE, RB = C::RB, NP = C::NP;
   const int tid = threadIdx.x;
@@ -90,7 +109,7 @@ fwd_kernel(FwdParams P) {
   float sc = P.scale_log2;
   float tau = P.rescale_log2;
   float out_mul = 1.f;
-  if constexpr (C::elt == Elt::FP8) {
+  if constexpr (FP8) {
     // descales fold into the score scale and the output; P is encoded as
     // e4m3(p * 448), which needs p <= 1, hence rescaling on every increase.
     // The exponent is offset by log2 448, so the exponentials yield p * 448
@@ -125,16 +144,10 @@ fwd_kernel(FwdParams P) {
   uint32_t koff[NP];
 #pragma unroll
   for (int p = 0; p < NP; ++p) koff[p] = tile_off<RB>(li, 2 * p + hf);
-  uint32_t voff[NE][2];
-  if constexpr (C::elt == Elt::BF16) {
+  uint32_t voff[NE];
+  if constexpr (FP8) {
 #pragma unroll
-    for (int e = 0; e < NE; ++e)
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-        voff[e][u] = tr16_off<RB, true>(lane, e, u);
-  } else if constexpr (C::elt == Elt::FP8) {
-#pragma unroll
-    for (int e = 0; e < NE; ++e) voff[e][0] = tr8_off<RB>(lane, e);
+    for (int e = 0; e < NE; ++e) voff[e] = tr8_off<RB>(lane, e);
   }
 
   f32x16 acc[NE];
@@ -156,6 +169,39 @@ fwd_kernel(FwdParams P) {
   }
   __syncthreads();
 
+  // e4m3 P.V for one 64-key chunk kc. RESIDUAL = false: P (from the scores s,
+  // already p * 448) encoded as e4m3, with the row sum of the unencoded values.
+  // RESIDUAL = true: a second pass for masked tiles that encodes what the
+  // first encoding rounded away, p * 448 - decode(e4m3(p * 448)), and adds its
+  // product with the same V^T operand.
+  auto pv_fp8 = [&](const f32x16 (&s)[NB], const char* vs, int kc, auto residual) __attribute__((always_inline)) {
+    constexpr bool RESIDUAL = decltype(residual)::value;
+    i32x8 pb;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const f32x16& sb = s[2 * kc + (j >> 2)];
+      const int o = (j & 3) * 4;
+      int w32 = cvt_fp8x2<false>(sb[o], sb[o + 1], 0);
+      w32 = cvt_fp8x2<true>(sb[o + 2], sb[o + 3], w32);
+      if constexpr (RESIDUAL) {
+        const auto d01 = __builtin_amdgcn_cvt_pk_f32_fp8(w32, false);
+        const auto d23 = __builtin_amdgcn_cvt_pk_f32_fp8(w32, true);
+        w32 = cvt_fp8x2<false>(sb[o] - d01[0], sb[o + 1] - d01[1], 0);
+        w32 = cvt_fp8x2<true>(sb[o + 2] - d23[0], sb[o + 3] - d23[1], w32);
+      } else {
+        l_part += (sb[o] + sb[o + 1]) + (sb[o + 2] + sb[o + 3]);
+      }
+      pb[j] = w32;
+    }
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      i32x2 a4[4];
+#pragma unroll
+      for (int wr = 0; wr < 4; ++wr) a4[wr] = lds_read_tr8(vs + voff[e] + (64 * kc + 16 * wr) * RB);
+      acc[e] = mfma_fp8(__builtin_bit_cast(i32x8, a4), pb, acc[e]);
+    }
+  };
+
   // One key/value tile. `cur` (being read) and `nxt` (being filled by the
   // LDS-DMA prefetch) are distinct stage buffers; declaring them restrict lets
   // the compiler see that the transposing reads of `cur` cannot depend on the
@@ -170,56 +216,32 @@ fwd_kernel(FwdParams P) {
     const char* vs = cur + C::TILE;
     if (key0 <= hi_w) {
       // ---- S^T = K Q^T ----
-      // K operands are read KLA pieces ahead into a register ring: the reads
-      // for piece p+KLA are issued before the MFMAs of piece p (scheduling
-      // barriers keep that order), so LDS latency hides behind KLA*NB MFMAs.
       f32x16 s[NB];
 #pragma unroll
       for (int b = 0; b < NB; ++b) s[b] = f32x16{};
-      if constexpr (C::elt == Elt::BF16) {
-        constexpr int KLA = 2;
-        i32x4 ka[KLA + 1][NB];
 #pragma unroll
-        for (int p = 0; p < KLA; ++p)
-#pragma unroll
-          for (int b = 0; b < NB; ++b) ka[p][b] = *reinterpret_cast<const i32x4*>(ks + koff[p] + 32 * b * RB);
+      for (int b = 0; b < NB; ++b) {
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-          if (p + KLA < NP) {
+          if constexpr (FP8) {
+            if (p & 1) continue;  // one MFMA per pair of 16-byte pieces (64 fp8 values)
+            const i32x4 a0 = *reinterpret_cast<const i32x4*>(ks + koff[p] + 32 * b * RB);
+            const i32x4 a1 = *reinterpret_cast<const i32x4*>(ks + koff[p + 1] + 32 * b * RB);
+            const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+            const i32x8 bq = {qf[p][0], qf[p][1], qf[p][2], qf[p][3],
+                              qf[p + 1][0], qf[p + 1][1], qf[p + 1][2], qf[p + 1][3]};
+            s[b] = mfma_fp8(a, bq, s[b]);
+          } else {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(ks + koff[p] + 32 * b * RB);
+            const f32x4 bq = __builtin_bit_cast(f32x4, qf[p]);
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
-              ka[(p + KLA) % (KLA + 1)][b] = *reinterpret_cast<const i32x4*>(ks + koff[p + KLA] + 32 * b * RB);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int b = 0; b < NB; ++b)
-            s[b] = mfma_bf16(__builtin_bit_cast(bf16x8, ka[p % (KLA + 1)][b]), __builtin_bit_cast(bf16x8, qf[p]), s[b]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      } else {
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-#pragma unroll
-          for (int p = 0; p < NP; ++p) {
-            if constexpr (C::elt == Elt::FP8) {
-              if (p & 1) continue;  // one MFMA per pair of 16-byte pieces (64 fp8 values)
-              const i32x4 a0 = *reinterpret_cast<const i32x4*>(ks + koff[p] + 32 * b * RB);
-              const i32x4 a1 = *reinterpret_cast<const i32x4*>(ks + koff[p + 1] + 32 * b * RB);
-              const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-              const i32x8 bq = {qf[p][0], qf[p][1], qf[p][2], qf[p][3],
-                                qf[p + 1][0], qf[p + 1][1], qf[p + 1][2], qf[p + 1][3]};
-              s[b] = mfma_fp8(a, bq, s[b]);
-            } else {
-              const f32x4 a = *reinterpret_cast<const f32x4*>(ks + koff[p] + 32 * b * RB);
-              const f32x4 bq = __builtin_bit_cast(f32x4, qf[p]);
-#pragma unroll
-              for (int u = 0; u < 4; ++u) s[b] = mfma_f32(a[u], bq[u], s[b]);
-            }
+            for (int u = 0; u < 4; ++u) s[b] = mfma_f32(a[u], bq[u], s[b]);
           }
         }
       }
       // ---- mask (causal diagonal, window start, ragged tail) and tile row max ----
-      if (kb.mask_tile<BN>(key0, qw)) {
+      const bool masked = kb.mask_tile<BN>(key0, qw);
+      if (masked) {
         // key key0 + 32b + 8(v/4) + 4h + v%4 is kept iff key_lo(qrow) <= key <= key_hi(qrow);
         // compare the lane-independent part r against two per-lane limits.
         const int hi = kb.hi(qrow) - key0 - 4 * hf, lo = kb.lo(qrow) - key0 - 4 * hf;
@@ -254,63 +276,18 @@ fwd_kernel(FwdParams P) {
         for (int e = 0; e < NE; ++e) acc[e] *= alpha;
       }
       // a row that has kept no key yet (m_ref = -inf, only under a window) gets p = 2^-inf = 0
-      const float neg_m = (m_ref == -INFINITY ? 0.f : -m_ref) + (C::elt == Elt::FP8 ? kLog2P8 : 0.f);
+      const float neg_m = (m_ref == -INFINITY ? 0.f : -m_ref) + (FP8 ? kLog2P8 : 0.f);
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int v = 0; v < 16; ++v) s[b][v] = fast_exp2(__builtin_fmaf(s[b][v], sc, neg_m));
       // ---- O^T += V^T P^T ----
-      if constexpr (C::elt == Elt::BF16) {
-        // V^T operands double-buffered like K above; four independent row-sum chains.
-        float l4[4] = {0.f, 0.f, 0.f, 0.f};
-        s16x4 va[2][NE][2];
+      if constexpr (FP8) {
 #pragma unroll
-        for (int e = 0; e < NE; ++e)
+        for (int kc = 0; kc < BN / 64; ++kc) pv_fp8(s, vs, kc, BoolTag<false>{});
+        if (masked) {
 #pragma unroll
-          for (int u = 0; u < 2; ++u) va[0][e][u] = lds_read_tr16(vs + voff[e][u]);
-#pragma unroll
-        for (int kc = 0; kc < BN / 16; ++kc) {
-          if (kc + 1 < BN / 16) {
-#pragma unroll
-            for (int e = 0; e < NE; ++e)
-#pragma unroll
-              for (int u = 0; u < 2; ++u) va[(kc + 1) & 1][e][u] = lds_read_tr16(vs + voff[e][u] + (kc + 1) * 16 * RB);
-          }
-          const f32x16& sb = s[kc >> 1];
-          const int o8 = (kc & 1) * 8;
-          bf16x8 pb;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) pb[i] = (__bf16)sb[o8 + i];
-          const i32x4 pw = __builtin_bit_cast(i32x4, pb);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) l4[i] = dot2_bf16_sum(pw[i], l4[i]);
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int e = 0; e < NE; ++e)
-            acc[e] = mfma_bf16(__builtin_bit_cast(bf16x8, va[kc & 1][e]), pb, acc[e]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        l_part += (l4[0] + l4[1]) + (l4[2] + l4[3]);
-      } else if constexpr (C::elt == Elt::FP8) {
-#pragma unroll
-        for (int kc = 0; kc < BN / 64; ++kc) {
-          i32x8 pb;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const f32x16& sb = s[2 * kc + (j >> 2)];
-            const int o = (j & 3) * 4;
-            l_part += (sb[o] + sb[o + 1]) + (sb[o + 2] + sb[o + 3]);
-            int w32 = cvt_fp8x2<false>(sb[o], sb[o + 1], 0);
-            w32 = cvt_fp8x2<true>(sb[o + 2], sb[o + 3], w32);
-            pb[j] = w32;
-          }
-#pragma unroll
-          for (int e = 0; e < NE; ++e) {
-            i32x2 a4[4];
-#pragma unroll
-            for (int wr = 0; wr < 4; ++wr) a4[wr] = lds_read_tr8(vs + voff[e][0] + (64 * kc + 16 * wr) * RB);
-            acc[e] = mfma_fp8(__builtin_bit_cast(i32x8, a4), pb, acc[e]);
-          }
+          for (int kc = 0; kc < BN / 64; ++kc) pv_fp8(s, vs, kc, BoolTag<true>{});
         }
       } else {
 #pragma unroll
@@ -363,7 +340,7 @@ fwd_kernel(FwdParams P) {
           *reinterpret_cast<bf16x4*>(orow + 32 * e + 8 * g + 4 * hf) = o4;
         }
     }
-    if (hf == 0) hr.lse[qrow] = (m_ref + __builtin_log2f(l_tot) - (C::elt == Elt::FP8 ? kLog2P8 : 0.f)) * kLn2;
+    if (hf == 0) hr.lse[qrow] = (m_ref + __builtin_log2f(l_tot) - (FP8 ? kLog2P8 : 0.f)) * kLn2;
   }
 }
 
@@ -668,11 +645,6 @@ fwd_pipe_kernel(FwdParams P) {
 // closing barrier. Each wave runs 1 + 2 (n_tiles + 1) barriers, a count fixed
 // by the workgroup's tile range alone.
 // ---------------------------------------------------------------------------
-template <bool B>
-struct BoolTag {
-  static constexpr bool value = B;
-};
-
 template <int D_, int BN_>
 struct FwdPPCfg {
   static constexpr int D = D_, BN = BN_, NW = 8;
