@@ -278,7 +278,7 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int D, int dtype, int variant)
  *                    are what fa_fwd returned for the same q, k, v.
  *   lse            : [B, H, N] float.
  *   dq, dk, dv     : [B, H, N, D] bfloat16 outputs.
- *   D              : 64 or 128.
+ *   D              : 64, 128 or 256.
  *   variant        : FA_BWD_ATOMIC -- one pass over key tiles computing dK, dV
  *                    and accumulating dQ with float atomics in the workspace
  *                    (the FlashAttention-2 scheme with scratch for atomics);

@@ -11,6 +11,7 @@ import pytest
 import torch
 
 from gpu_util import TOL_BF16_GRAD, grad_err, max_abs, prepare, rel_fro, to_f64
+from gpu_util import sample_rows
 from oracle import attention
 from tiled_online_softmax_amd import fa, inputs
 
@@ -49,7 +50,7 @@ def test_bwd_causal_workload_full(variant):
 
 
 @pytest.mark.parametrize("variant", sorted(VARIANTS))
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_small_shapes(variant, D, causal):
     for i, N in enumerate([1, 2, 17, 28, 29, 30, 31, 63, 65, 129, 300]):
@@ -88,8 +89,9 @@ def test_deterministic_variant_is_bitwise_stable():
             assert torch.equal(a, b)
 
 
-def test_variants_agree():
-    dev, _ = prepare("bf16", (1, 2, 900, 128), 6, with_grad=True)
+@pytest.mark.parametrize("D", [128, 256])
+def test_variants_agree(D):
+    dev, _ = prepare("bf16", (1, 2, 900, D), 6, with_grad=True)
     ga = _grads(dev, True, 0.1, fa.FA_BWD_ATOMIC)
     gd = _grads(dev, True, 0.1, fa.FA_BWD_DETERMINISTIC)
     # The variants use different key-pass tilings and query-tile orders, so dK and dV differ only by
@@ -111,3 +113,31 @@ def test_dkdv_only_matches_full_backward():
         dk2, dv2 = fa.bwd_dkdv(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, causal=causal)
         torch.cuda.synchronize()
         assert torch.equal(dk, dk2) and torch.equal(dv, dv2)
+
+
+_D256_REF = {}
+
+
+@pytest.mark.parametrize("variant", sorted(VARIANTS))
+def test_bwd_d256_causal_workload(variant):
+    """B=1 H=8 N=8192 D=256 bf16 x0.5 causal (the large-head-dim workload's shape and values, causal): dQ on
+    sampled rows of every head, and every element of dQ, dK and dV of two heads."""
+    w = inputs.WORKLOADS["bwd_d256_bf16"]
+    dev, ref = prepare("bf16", w.shape, w.seed, w.multiplier, with_grad=True)
+    o, lse = fa.fwd(dev["q"], dev["k"], dev["v"], causal=w.causal, scale=w.scale)
+    dq, dk, dv = fa.bwd(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, causal=w.causal, scale=w.scale,
+                        variant=VARIANTS[variant])
+    torch.cuda.synchronize()
+    rows = sample_rows(w.N)
+    if "dq_rows" not in _D256_REF:
+        _D256_REF["dq_rows"] = attention.backward_dq_rows(ref["q"], ref["k"], ref["v"], ref["do"], w.causal, w.scale,
+                                                          rows)
+    e = grad_err(to_f64(dq)[:, :, rows], _D256_REF["dq_rows"])
+    print(f"[{w.name} {variant}] dQ on {len(rows)} rows of every head: {e:.3e}", flush=True)
+    assert e <= TOL_BF16_GRAD
+    for h in (0, 5):
+        sl = (slice(0, 1), slice(h, h + 1))
+        if h not in _D256_REF:
+            _D256_REF[h] = attention.backward(ref["q"][sl], ref["k"][sl], ref["v"][sl], ref["do"][sl], w.causal,
+                                              w.scale)
+        _check([to_f64(x)[sl] for x in (dq, dk, dv)], _D256_REF[h], f"{w.name} {variant} head {h}")

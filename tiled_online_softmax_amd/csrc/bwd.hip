@@ -749,7 +749,7 @@ static hipError_t launch_bwd(int variant, const BwdParams& p, int B, int H, hipS
   return hipGetLastError();
 }
 
-bool bwd_supported(int D) { return D == 64 || D == 128; }
+bool bwd_supported(int D) { return D == 64 || D == 128 || D == 256; }
 
 // Parameter table for the backward: D -> key pass with atomic dQ (waves,
 // query tile, waves per SIMD), key pass without, and the dQ pass (waves, key
@@ -763,6 +763,8 @@ hipError_t bwd_dispatch(int D, int variant, const BwdParams& p, int B, int H, hi
     return launch_bwd<DkdvCfg<64, 4, 64, 2>, DkdvCfg<64, 4, 32, 3>, DqCfg<64, 4, 32, 3>>(variant, p, B, H, st);
   if (D == 128)
     return launch_bwd<DkdvCfg<128, 4, 64, 1>, DkdvCfg<128, 4, 32, 2>, DqCfg<128, 4, 64, 2>>(variant, p, B, H, st);
+  if (D == 256)
+    return launch_bwd<DkdvCfg<256, 4, 32, 1>, DkdvCfg<256, 4, 32, 1>, DqCfg<256, 4, 32, 1>>(variant, p, B, H, st);
   return hipErrorInvalidValue;
 }
 

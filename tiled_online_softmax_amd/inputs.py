@@ -121,6 +121,9 @@ WORKLOADS: Dict[str, Workload] = {
     "d256_bf16": Workload("d256_bf16", 1, 8, 8192, 256, "bf16", False, "fwd", multiplier=0.5, seed=SEED_BASE + 3),
     "bwd_causal_bf16": Workload("bwd_causal_bf16", 2, 16, 4096, 64, "bf16", True, "bwd", seed=SEED_BASE + 4),
     "long_fp8_causal": Workload("long_fp8_causal", 1, 32, 32768, 128, "fp8", True, "fwd", seed=SEED_BASE + 5),
+    # The backward at the largest head dimension: the large-head-dim workload's shape and values, causal.
+    "bwd_d256_bf16": Workload("bwd_d256_bf16", 1, 8, 8192, 256, "bf16", True, "bwd", multiplier=0.5,
+                              seed=SEED_BASE + 11),
     # Grouped-query attention (a NEXT-row extension): 32 query heads sharing 8 K/V heads.
     "gqa_causal_bf16": Workload("gqa_causal_bf16", 4, 32, 2048, 128, "bf16", True, "fwd+bwd", seed=SEED_BASE + 6,
                                 hkv=8),
