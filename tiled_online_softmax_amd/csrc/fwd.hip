@@ -953,7 +953,11 @@ hipError_t fwd_dispatch(Elt e, int D, const FwdParams& p, int B, int H, hipStrea
           return launch_fwd_pp<FwdPPCfg<128, 64>>(p, B, H, st);
         return launch_fwd_pipe<FwdDCfg<Elt::BF16, 128, 64, 4, 2>>(p, B, H, st);
       }
-      if (D == 256) return launch_fwd_pipe<FwdDCfg<Elt::BF16, 256, 64, 4, 1>>(p, B, H, st);
+      if (D == 256) {
+        // two waves per SIMD with O in AGPRs (fwd_lean.hip), except block-sparse launches
+        if (!p.kv_index) return fwd_lean_dispatch(256, p, B, H, st);
+        return launch_fwd_pipe<FwdDCfg<Elt::BF16, 256, 64, 4, 1>>(p, B, H, st);
+      }
       break;
     case Elt::FP8:
       // e4m3 operands need few registers (105 / 154 VGPRs): four and three waves per SIMD

@@ -131,6 +131,8 @@ struct KeyTiles {
 };
 
 bool fwd_supported(Elt e, int D);
+// bf16 forward with O in AGPRs at two waves per SIMD (fwd_lean.hip), D = 256.
+hipError_t fwd_lean_dispatch(int D, const FwdParams& p, int B, int H, hipStream_t st);
 // H: query heads; K and V have H / p.group heads.
 hipError_t fwd_dispatch(Elt e, int D, const FwdParams& p, int B, int H, hipStream_t st);
 
