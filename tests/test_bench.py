@@ -21,12 +21,15 @@ def test_more_than_one_gpu_exits_with_a_message(n):
 
 
 def test_cpu_baseline_times_the_oracle():
-    """One head of the step workload: the oracle's forward + backward, reported with its sample and cores."""
-    w = inputs.WORKLOADS["mh_causal_bf16"]
-    rec = bench.cpu_baseline(w, w.fwd_flops() + w.bwd_flops(), heads=1)
+    """A sample of the step's workload (reduced here to H=4, N=1024): the oracle's forward of two heads on its
+    own dequantised e4m3 inputs, reported with the sample and the cores."""
+    import dataclasses
+
+    w = dataclasses.replace(inputs.WORKLOADS["long_fp8_causal"], H=4, N=1024)
+    rec = bench.cpu_baseline(w, inputs.make(w, with_grad=False))
     assert rec["kind"] == "oracle" and rec["unit"] == "TFLOP/s"
     assert rec["value"] > 0 and rec["cores"] >= 1
-    assert "1 of 64" in rec["sample"]
+    assert "2 of the 4" in rec["sample"] and "all 1024 query rows" in rec["sample"]
 
 
 def test_code_hash_ignores_comments_and_blank_lines(tmp_path):
