@@ -80,7 +80,7 @@ enum { FA_BWD_ATOMIC = 0, FA_BWD_DETERMINISTIC = 1 };
  *   causal  : 1 keeps key j only for query i >= j.
  *   scale   : factor on q.k, > 0 and finite (usually 1/sqrt(D)).
  * Rows are rescaled when their running max grows by more than 8 in base-2
- * units (FA_FP8_E4M3: whenever it grows), which is exact in exact arithmetic.
+ * units (FA_FP8_E4M3: by more than 2), which is exact in exact arithmetic.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int D, int causal, float scale, int dtype,
@@ -217,8 +217,9 @@ int fa_fwd_sparse(const void* q, const void* k, const void* v, void* o,
  * fa_fwd with an explicit conditional-rescale threshold `rescale_log2`
  * (>= 0, in base-2 units of the score): a row's reference max is moved --
  * and its accumulator rescaled -- only when a new tile's max exceeds it by
- * more than this. 0 rescales on every increase. Ignored (forced to 0) for
- * FA_FP8_E4M3, whose probabilities must stay <= 1 to fit the e4m3 range.
+ * more than this. 0 rescales on every increase. Ignored for FA_FP8_E4M3,
+ * which fixes it at 2: probabilities up to 4 are encoded as e4m3(p * 112),
+ * which stays within e4m3's largest value 448.
  * The result is the same attention for every threshold (the conditional
  * rescaling of page "r/mlscaling", FA4 bullet, and of the FlashAttention-4
  * entry on the page "FlashAttention" entity trail, section "Corpus findings").
@@ -239,12 +240,13 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
  *   o        : [B, H, N, D] bfloat16; lse: [B, H, N] float.
  *   D        : 64 or 128.
  * Both products use fp8 MFMA, with the descales folded into the score scale
- * and the output. The probabilities are encoded as e4m3(p * 448) for the P.V
- * product while the row sums and lse use the unencoded float32 p. On key
- * tiles that need masking (the causal diagonal, a ragged tail) -- which hold
- * every key of the shortest rows -- a second e4m3 term carries the rounding
- * residual of the first, so those products see about 2^-8 relative error in
- * P instead of up to 2^-4.
+ * and the output. The probabilities are encoded as e4m3(p * 112) (p <= 4:
+ * the rescale threshold is 2) for the P.V product, and the row sums that
+ * normalise O and enter lse add the same encoded values, on the matrix core.
+ * On key tiles that need masking (the causal diagonal, a ragged tail) --
+ * which hold every key of the shortest rows -- a second e4m3 term carries the
+ * rounding residual of the first, so those products see about 2^-8 relative
+ * error in P instead of up to 2^-4.
  */
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int N, int D, int causal, float scale,

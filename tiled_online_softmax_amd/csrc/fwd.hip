@@ -42,7 +42,9 @@ struct BoolTag {
 //   * e4m3: both products run on the 32x32x64 fp8 MFMA. The descales fold
 //     into the score scale and the output; V^T operands are read with
 //     transposing 8-bit LDS reads (ds_read_b64_tr_b8); P is encoded as
-//     e4m3(p * 448), the exponentials taking log2 448 into their offset. e4m3
+//     e4m3(p * 112), the exponentials taking log2 112 into their offset, so a
+//     row's reference max may trail its true max by up to 2 (base 2) before
+//     the accumulator must be rescaled (p <= 4 still fits e4m3's 448). e4m3
 //     keeps 3 significand bits, so an encoded probability is off by up to 2^-4
 //     of itself, and a row whose keys all sit in one or two tiles would carry
 //     that into O almost undiluted. On tiles that need masking (the causal
@@ -52,8 +54,10 @@ struct BoolTag {
 // The tile loop is unrolled by two so the stage base of every LDS read is an
 // immediate.
 // ---------------------------------------------------------------------------
-// log2(448): e4m3's largest finite value is 448; P is encoded as e4m3(p * 448).
-constexpr float kLog2P8 = 8.80735492205760410744f;
+// e4m3's largest finite value is 448 = 4 * 112; P is encoded as e4m3(p * 112)
+// for p <= 2^kTauP8 = 4, which fixes the rescale threshold at kTauP8.
+constexpr float kTauP8 = 2.f;
+constexpr float kLog2P8 = 6.80735492205760410744f;  // log2(112)
 
 template <Elt E, int D_, int BN_, int NW_, int OCC_>
 struct FwdDCfg {
@@ -111,8 +115,8 @@ fwd_kernel(FwdParams P) {
   float out_mul = 1.f;
   if constexpr (FP8) {
     // descales fold into the score scale and the output; P is encoded as
-    // e4m3(p * 448), which needs p <= 1, hence rescaling on every increase.
-    // The exponent is offset by log2 448, so the exponentials yield p * 448
+    // e4m3(p * 112), which needs p <= 4, hence the threshold kTauP8 = 2.
+    // The exponent is offset by log2 112, so the exponentials yield p * 112
     // directly; the float32 row sum then also carries the factor, which
     // cancels in O and is taken out of lse.
     const float dq = P.q_descale ? *P.q_descale : 1.f;
@@ -120,7 +124,7 @@ fwd_kernel(FwdParams P) {
     const float dv = P.v_descale ? *P.v_descale : 1.f;
     sc *= dq * dk;
     out_mul = dv;
-    tau = 0.f;
+    tau = kTauP8;
   }
 
   // Loader: 16-byte slot `lane` of 1 KB block m of a tile comes from tile_pos(slot).
@@ -154,6 +158,19 @@ fwd_kernel(FwdParams P) {
 #pragma unroll
   for (int e = 0; e < NE; ++e) acc[e] = f32x16{};
   float m_ref = -INFINITY, l_part = 0.f;
+  // e4m3: the row sums run on the matrix core. A 16x16x128 MFMA contracts the
+  // P operand of the 32x32x64 product (lane L: query row L % 32, 32 of the 64
+  // keys) against a 0 / 1 pattern that adds, for output lane l, the four
+  // operand lanes of row l % 32 (lane groups of 16 with the parity of l / 16):
+  // every lane receives its row's sum of the encoded probabilities, exactly the
+  // weights P.V used, in all four accumulator entries.
+  f32x4 l_acc = {0.f, 0.f, 0.f, 0.f};
+  i32x8 ones_sel;
+  if constexpr (FP8) {
+    const int v = ((lane >> 2) & 1) == ((lane >> 4) & 1) ? 0x38383838 : 0;  // e4m3 1.0 = 0x38
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ones_sel[i] = v;
+  }
 
   // The workgroup's key tiles, j = 0 .. n_tiles-1: dense, the tiles
   // [t_lo, t_end) that hold every key a row of it keeps; sparse, the tiles of
@@ -170,10 +187,10 @@ fwd_kernel(FwdParams P) {
   __syncthreads();
 
   // e4m3 P.V for one 64-key chunk kc. RESIDUAL = false: P (from the scores s,
-  // already p * 448) encoded as e4m3, with the row sum of the unencoded values.
-  // RESIDUAL = true: a second pass for masked tiles that encodes what the
-  // first encoding rounded away, p * 448 - decode(e4m3(p * 448)), and adds its
-  // product with the same V^T operand.
+  // already p * 112) encoded as e4m3. RESIDUAL = true: a second pass for masked
+  // tiles that encodes what the first encoding rounded away,
+  // p * 112 - decode(e4m3(p * 112)), and adds its product with the same V^T
+  // operand. Both add their encoded row sums to l_acc.
   auto pv_fp8 = [&](const f32x16 (&s)[NB], const char* vs, int kc, auto residual) __attribute__((always_inline)) {
     constexpr bool RESIDUAL = decltype(residual)::value;
     i32x8 pb;
@@ -188,11 +205,10 @@ fwd_kernel(FwdParams P) {
         const auto d23 = __builtin_amdgcn_cvt_pk_f32_fp8(w32, true);
         w32 = cvt_fp8x2<false>(sb[o] - d01[0], sb[o + 1] - d01[1], 0);
         w32 = cvt_fp8x2<true>(sb[o + 2] - d23[0], sb[o + 3] - d23[1], w32);
-      } else {
-        l_part += (sb[o] + sb[o + 1]) + (sb[o + 2] + sb[o + 3]);
       }
       pb[j] = w32;
     }
+    l_acc = mfma_fp8_16(ones_sel, pb, l_acc);
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
       i32x2 a4[4];
@@ -271,7 +287,10 @@ fwd_kernel(FwdParams P) {
         // rows that do not grow keep their scale (also when m_ref is still -inf: -inf - -inf is NaN)
         const float alpha = grow ? fast_exp2(m_ref - m_new) : 1.f;
         m_ref = m_new;
-        l_part *= alpha;
+        if constexpr (FP8)
+          l_acc *= alpha;
+        else
+          l_part *= alpha;
 #pragma unroll
         for (int e = 0; e < NE; ++e) acc[e] *= alpha;
       }
@@ -317,7 +336,7 @@ fwd_kernel(FwdParams P) {
 
   // ---- epilogue: O = acc / l, lse = ln(sum exp(s)) ----
   // A row that kept no key has l = 0 and m_ref = -inf: O = 0 and lse = -inf.
-  const float l_tot = pair_sum32(l_part);
+  const float l_tot = FP8 ? l_acc[0] : pair_sum32(l_part);
   const float inv = l_tot > 0.f ? out_mul / l_tot : 0.f;
   if (qrow < N) {
     if constexpr (C::elt == Elt::F32) {
