@@ -158,6 +158,7 @@ fwd_kernel(FwdParams P) {
 #pragma unroll
   for (int e = 0; e < NE; ++e) acc[e] = f32x16{};
   float m_ref = -INFINITY, l_part = 0.f;
+  float neg_m = FP8 ? kLog2P8 : 0.f;  // exponent offset of p: -m_ref (0 while m_ref = -inf), + log2 112 for e4m3
   // e4m3: the row sums run on the matrix core. A 16x16x128 MFMA contracts the
   // P operand of the 32x32x64 product (lane L: query row L % 32, 32 of the 64
   // keys) against a 0 / 1 pattern that adds, for output lane l, the four
@@ -166,6 +167,11 @@ fwd_kernel(FwdParams P) {
   // weights P.V used, in all four accumulator entries.
   f32x4 l_acc = {0.f, 0.f, 0.f, 0.f};
   i32x8 ones_sel;
+  // e4m3 P operand. Each word is written by two half-word packs, the first of
+  // which keeps the other half of its `old` operand: passing the previous
+  // tile's word there (overwritten anyway) keeps the words in place without
+  // zeroing moves.
+  i32x8 pb = {};
   if constexpr (FP8) {
     const int v = ((lane >> 2) & 1) == ((lane >> 4) & 1) ? 0x38383838 : 0;  // e4m3 1.0 = 0x38
 #pragma unroll
@@ -193,17 +199,16 @@ fwd_kernel(FwdParams P) {
   // operand. Both add their encoded row sums to l_acc.
   auto pv_fp8 = [&](const f32x16 (&s)[NB], const char* vs, int kc, auto residual) __attribute__((always_inline)) {
     constexpr bool RESIDUAL = decltype(residual)::value;
-    i32x8 pb;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const f32x16& sb = s[2 * kc + (j >> 2)];
       const int o = (j & 3) * 4;
-      int w32 = cvt_fp8x2<false>(sb[o], sb[o + 1], 0);
+      int w32 = cvt_fp8x2<false>(sb[o], sb[o + 1], pb[j]);
       w32 = cvt_fp8x2<true>(sb[o + 2], sb[o + 3], w32);
       if constexpr (RESIDUAL) {
         const auto d01 = __builtin_amdgcn_cvt_pk_f32_fp8(w32, false);
         const auto d23 = __builtin_amdgcn_cvt_pk_f32_fp8(w32, true);
-        w32 = cvt_fp8x2<false>(sb[o] - d01[0], sb[o + 1] - d01[1], 0);
+        w32 = cvt_fp8x2<false>(sb[o] - d01[0], sb[o + 1] - d01[1], w32);
         w32 = cvt_fp8x2<true>(sb[o + 2] - d23[0], sb[o + 3] - d23[1], w32);
       }
       pb[j] = w32;
@@ -287,6 +292,8 @@ fwd_kernel(FwdParams P) {
         // rows that do not grow keep their scale (also when m_ref is still -inf: -inf - -inf is NaN)
         const float alpha = grow ? fast_exp2(m_ref - m_new) : 1.f;
         m_ref = m_new;
+        // a row that has kept no key yet (m_ref = -inf, only under a window) gets p = 2^-inf = 0
+        neg_m = (m_ref == -INFINITY ? 0.f : -m_ref) + (FP8 ? kLog2P8 : 0.f);
         if constexpr (FP8)
           l_acc *= alpha;
         else
@@ -294,8 +301,6 @@ fwd_kernel(FwdParams P) {
 #pragma unroll
         for (int e = 0; e < NE; ++e) acc[e] *= alpha;
       }
-      // a row that has kept no key yet (m_ref = -inf, only under a window) gets p = 2^-inf = 0
-      const float neg_m = (m_ref == -INFINITY ? 0.f : -m_ref) + (FP8 ? kLog2P8 : 0.f);
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
