@@ -984,7 +984,7 @@ hipError_t fwd_dispatch(Elt e, int D, const FwdParams& p, int B, int H, hipStrea
       }
       break;
     case Elt::FP8:
-      // e4m3 operands need few registers (105 / 154 VGPRs): four and three waves per SIMD
+      // e4m3 operands need few registers (121 / 166 VGPRs): four and three waves per SIMD
       if (D == 64) return launch_fwd_direct<FwdDCfg<Elt::FP8, 64, 64, 4, 4>>(p, B, H, st);
       if (D == 128) return launch_fwd_direct<FwdDCfg<Elt::FP8, 128, 64, 4, 3>>(p, B, H, st);
       break;
