@@ -16,7 +16,8 @@ from typing import Optional, Tuple
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+# FA_LIBRARY selects another build of the library (e.g. the host-sanitised one, see build.py).
+LIB_PATH = os.environ.get("FA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_F32, FA_BF16, FA_FP8_E4M3 = 0, 1, 2
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, 1, 2, 3, 4
