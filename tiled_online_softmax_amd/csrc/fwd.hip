@@ -96,7 +96,8 @@ fwd_kernel(FwdParams P) {
   // Workgroup -> (head, query tile); under causal masking the last query
   // tiles carry the most key tiles, so rank 0 is the last one.
   int bh, qt;
-  wg_map(P.n_qtiles, rank_major(P.cu_q != nullptr || P.kv_index != nullptr, P.causal, P.window, min(P.N, P.Nk), true), P.group, bh, qt);
+  wg_map(P.n_qtiles, rank_major(P.cu_q != nullptr || P.kv_index != nullptr, P.causal, P.window, min(P.N, P.Nk), true), P.group, bh, qt,
+         long_causal_forward(P.cu_q != nullptr || P.kv_index != nullptr, P.causal, P.window));
   const HeadRows hr = head_rows<C::ESZ>(P, bh);
   const int N = hr.nq;
   const int n_qt = (N + C::BM - 1) / C::BM;  // this entry's query tiles (fewer for a short packed sequence)
@@ -399,7 +400,8 @@ fwd_pipe_kernel(FwdParams P) {
   const int li = lane & 31, hf = lane >> 5;
 
   int bh, qt;
-  wg_map(P.n_qtiles, rank_major(P.cu_q != nullptr || P.kv_index != nullptr, P.causal, P.window, min(P.N, P.Nk), true), P.group, bh, qt);
+  wg_map(P.n_qtiles, rank_major(P.cu_q != nullptr || P.kv_index != nullptr, P.causal, P.window, min(P.N, P.Nk), true), P.group, bh, qt,
+         long_causal_forward(P.cu_q != nullptr || P.kv_index != nullptr, P.causal, P.window));
   const HeadRows hr = head_rows<2>(P, bh);
   const int N = hr.nq;
   const int n_qt = (N + C::BM - 1) / C::BM;
@@ -697,7 +699,8 @@ fwd_pp_kernel(FwdParams P) {
   const bool second = wave >= 4;  // the second group runs half a step behind the first
 
   int bh, qt;
-  wg_map(P.n_qtiles, rank_major(P.cu_q != nullptr || P.kv_index != nullptr, P.causal, P.window, min(P.N, P.Nk), true), P.group, bh, qt);
+  wg_map(P.n_qtiles, rank_major(P.cu_q != nullptr || P.kv_index != nullptr, P.causal, P.window, min(P.N, P.Nk), true), P.group, bh, qt,
+         long_causal_forward(P.cu_q != nullptr || P.kv_index != nullptr, P.causal, P.window));
   const HeadRows hr = head_rows<2>(P, bh);
   const int N = hr.nq;
   const int n_qt = (N + C::BM - 1) / C::BM;

@@ -94,7 +94,8 @@ fwd_lean_kernel(FwdParams P) {
   const int li = lane & 31, hf = lane >> 5;
 
   int bh, qt;
-  wg_map(P.n_qtiles, rank_major(P.cu_q != nullptr, P.causal, P.window, min(P.N, P.Nk), true), P.group, bh, qt);
+  wg_map(P.n_qtiles, rank_major(P.cu_q != nullptr, P.causal, P.window, min(P.N, P.Nk), true), P.group, bh, qt,
+         long_causal_forward(P.cu_q != nullptr, P.causal, P.window));
   const HeadRows hr = head_rows<2>(P, bh);
   const int N = hr.nq;
   const int n_qt = (N + C::BM - 1) / C::BM;
