@@ -243,10 +243,8 @@ bwd_dkdv_kernel(BwdParams P, int n_ktiles) {
   // leave the first keys with no query at all: then dK = dV = 0.
   static_assert(!SPARSE || C::BK == kBlock, "a key tile is one mask block");
   QueryTiles<SPARSE, BQ> qts(P, bb * P.hq + h0, kt, qt0, nq, group);
-  if (qts.valid()) {
-    issue(qts.g, qts.row(), smem);
-    wait_vmem();
-  }
+  if (qts.valid()) issue(qts.g, qts.row(), smem);
+  wait_vmem();  // unconditional: no path reaches the tile loop with the register loads above pending
   __syncthreads();
 
   // One query tile. `cur` is read while the LDS-DMA prefetch fills `nxt`; the
@@ -563,10 +561,8 @@ bwd_dq_kernel(BwdParams P, int n_qtiles) {
   const KeyTiles<SPARSE, BN> ts(P, bh, kb, q0, q0 + C::BM);
   const int n_tiles = ts.n;
 
-  if (n_tiles > 0) {
-    issue(ts.at_clamped(0) * BN, smem);
-    wait_vmem();
-  }
+  if (n_tiles > 0) issue(ts.at_clamped(0) * BN, smem);
+  wait_vmem();  // unconditional: no path reaches the tile loop with the register loads above pending
   __syncthreads();
 
   // One key tile; see the key-tile pass for the restrict qualifiers.

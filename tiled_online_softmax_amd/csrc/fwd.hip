@@ -187,10 +187,10 @@ fwd_kernel(FwdParams P) {
   const int n_tiles = ts.n;
   const int hi_w = kb.hi(qw + 31);
 
-  if (n_tiles > 0) {
-    issue(ts.at_clamped(0) * BN, smem);
-    wait_vmem();
-  }
+  if (n_tiles > 0) issue(ts.at_clamped(0) * BN, smem);
+  // unconditional: a path that reached the tile loop with the Q loads pending
+  // would make the compiler wait for every prefetch inside the loop
+  wait_vmem();
   __syncthreads();
 
   // e4m3 P.V for one 64-key chunk kc. RESIDUAL = false: P (from the scores s,

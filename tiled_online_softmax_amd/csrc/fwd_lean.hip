@@ -141,10 +141,8 @@ fwd_lean_kernel(FwdParams P) {
   const int n_tiles = ts.n;
   const int hi_w = kb.hi(qw + 31);
 
-  if (n_tiles > 0) {
-    issue(ts.at(0) * BN, smem);
-    wait_vmem();
-  }
+  if (n_tiles > 0) issue(ts.at(0) * BN, smem);
+  wait_vmem();  // unconditional: no path reaches the tile loop with the Q loads pending
   __syncthreads();
 
   auto tile = [&](int j, const char* __restrict__ cur, char* __restrict__ nxt) __attribute__((always_inline)) {
