@@ -124,3 +124,19 @@ def test_gqa_workload_bwd_two_groups():
                                    ref["do"][b:b + 1, qs], w.causal, w.scale)
         mine = [to_f64(g[0][b:b + 1, qs]), to_f64(g[1][b:b + 1, kh:kh + 1]), to_f64(g[2][b:b + 1, kh:kh + 1])]
         _check_grads(mine, g_ref, f"{w.name} bwd b{b} kv{kh}", G)
+
+
+def test_gqa_long_causal_forward_sampled_rows():
+    """B=1 H=32 (8 K/V heads) N=32768 D=64 bf16 causal: 256 query tiles per head, so the launch takes the
+    order of long causal forwards (each XCD runs its K/V groups one after another, the four query heads of a
+    group together); sampled rows of every head."""
+    N = 32768
+    dev, ref = prepare("bf16", (1, 32, N, 64), 9100, hkv=8)
+    o, lse = fa.fwd(dev["q"], dev["k"], dev["v"], causal=True)
+    torch.cuda.synchronize()
+    rows = sample_rows(N)
+    o_ref, lse_ref = attention.forward(ref["q"], ref["k"], ref["v"], True, 1.0 / 8.0, rows=rows)
+    og, lg = to_f64(o)[:, :, rows], to_f64(lse)[:, :, rows]
+    eo, el, rf = max_abs(og, o_ref), max_abs(lg, lse_ref), rel_fro(og, o_ref)
+    print(f"[gqa long fwd H32/8 N{N} D64] O {eo:.3e} lse {el:.3e} rel {rf:.3e}", flush=True)
+    assert eo <= TOL_BF16_O and el <= TOL_BF16_LSE and rf <= REL_BF16
