@@ -100,3 +100,70 @@ def test_fp8_unit_descales_via_fa_fwd():
     torch.cuda.synchronize()
     o_ref, lse_ref = attention.forward(*[codecs.e4m3_to_f64(c) for c in codes], False, 0.125)
     assert max_abs(to_f64(o), o_ref) <= TOL_FP8 and max_abs(to_f64(lse), lse_ref) <= TOL_FP8
+
+
+def _codes(rng, shape):
+    """e4m3 codes of N(0, 1) draws (unit descales): host codes and the device tensor."""
+    c = codecs.f64_to_e4m3(rng.standard_normal(shape))
+    return c, torch.from_numpy(c).to(DEV)
+
+
+# (H, Hkv, Nq, Nk, D, causal, window): grouped K/V heads, unequal lengths (causal aligned at the bottom
+# right), a sliding window, ragged tails on both sides and a query block longer than the keys
+GENERAL = [(4, 2, 200, 333, 64, True, -1), (4, 1, 333, 200, 128, True, -1), (8, 2, 257, 257, 128, True, 64),
+           (2, 2, 130, 515, 128, False, 100), (6, 3, 77, 1000, 64, False, -1), (4, 4, 600, 129, 128, True, 0)]
+
+
+@pytest.mark.parametrize("H,Hkv,Nq,Nk,D,causal,window", GENERAL)
+def test_fp8_general_layouts(H, Hkv, Nq, Nk, D, causal, window):
+    """fa_fwd_general with FA_FP8_E4M3 codes (descales 1) against the oracle on the decoded values."""
+    rng = np.random.default_rng(7800 + H + Hkv + Nq + Nk + D + window)
+    (qc, qd), (kc, kd), (vc, vd) = (_codes(rng, (2, h, n, D)) for h, n in ((H, Nq), (Hkv, Nk), (Hkv, Nk)))
+    scale = 1 / math.sqrt(D)
+    o, lse = fa.fwd(qd, kd, vd, causal=causal, scale=scale, window=None if window < 0 else window)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = attention.forward(*(codecs.e4m3_to_f64(c) for c in (qc, kc, vc)), causal, scale, window=window)
+    live = lse_ref != -np.inf
+    og, lg = to_f64(o), to_f64(lse)
+    assert np.all(og[~live] == 0) and np.all(lg[~live] == -np.inf)
+    eo, el = max_abs(og, o_ref), max_abs(lg[live], lse_ref[live])
+    print(f"[fp8 general H{H}/{Hkv} Nq{Nq} Nk{Nk} D{D} causal={causal} window={window}] O {eo:.3e} lse {el:.3e}",
+          flush=True)
+    assert eo <= TOL_FP8 and el <= TOL_FP8
+
+
+def test_fp8_strided_views():
+    """The e4m3 forward on [B, N, H, D] storage seen as [B, H, N, D] views (fa_fwd_strided), grouped K/V heads."""
+    rng = np.random.default_rng(7850)
+    B, H, Hkv, Nq, Nk, D = 2, 4, 2, 190, 300, 128
+    (qc, qd), (kc, kd), (vc, vd) = (_codes(rng, (B, n, h, D)) for h, n in ((H, Nq), (Hkv, Nk), (Hkv, Nk)))
+    o = torch.empty((B, Nq, H, D), dtype=torch.bfloat16, device=DEV).transpose(1, 2)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=DEV)
+    fa.fwd(qd.transpose(1, 2), kd.transpose(1, 2), vd.transpose(1, 2), causal=True, scale=0.1, out=o, lse=lse)
+    torch.cuda.synchronize()
+    vals = [codecs.e4m3_to_f64(c).transpose(0, 2, 1, 3) for c in (qc, kc, vc)]
+    o_ref, lse_ref = attention.forward(*vals, True, 0.1)
+    assert max_abs(to_f64(o), o_ref) <= TOL_FP8 and max_abs(to_f64(lse), lse_ref) <= TOL_FP8
+
+
+def test_fp8_varlen():
+    """The packed variable-length forward on e4m3 codes: empty, one-row and ragged sequences, grouped heads."""
+    rng = np.random.default_rng(7900)
+    lq, lk = [0, 1, 130, 77, 300], [5, 1, 200, 0, 300]
+    cu_q, cu_k = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    H, Hkv, D = 4, 2, 64
+    (qc, qd), (kc, kd), (vc, vd) = (_codes(rng, (t, h, D)) for t, h in ((cu_q[-1], H), (cu_k[-1], Hkv),
+                                                                          (cu_k[-1], Hkv)))
+    cq, ck = (torch.from_numpy(c.astype(np.int32)).to(DEV) for c in (cu_q, cu_k))
+    for causal, window in ((False, -1), (True, -1), (True, 50)):
+        o, lse = fa.fwd_varlen(qd, kd, vd, cq, ck, max(lq), max(lk), causal=causal, scale=0.125,
+                               window=None if window < 0 else window)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = attention.forward_varlen(*(codecs.e4m3_to_f64(c) for c in (qc, kc, vc)), cu_q, cu_k,
+                                                  causal, 0.125, window=window)
+        live = lse_ref != -np.inf
+        og, lg = to_f64(o), to_f64(lse)
+        assert np.all(lg[~live] == -np.inf) and np.all(og.transpose(1, 0, 2)[~live] == 0)
+        eo, el = max_abs(og, o_ref), max_abs(lg[live], lse_ref[live])
+        print(f"[fp8 varlen causal={causal} window={window}] O {eo:.3e} lse {el:.3e}", flush=True)
+        assert eo <= TOL_FP8 and el <= TOL_FP8
