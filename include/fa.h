@@ -75,8 +75,7 @@ enum { FA_BWD_ATOMIC = 0, FA_BWD_DETERMINISTIC = 1 };
  *   o       : [B, H, N, D] output; float for FA_F32, bfloat16 otherwise.
  *   lse     : [B, H, N] float output, natural-log logsumexp of the scaled
  *             scores of each query row (what fa_bwd consumes).
- *   D       : head dimension; FA_F32 and FA_BF16 support 64, 128 and 256,
- *             FA_FP8_E4M3 supports 64 and 128.
+ *   D       : head dimension: 64, 128 or 256 (every dtype).
  *   causal  : 1 keeps key j only for query i >= j.
  *   scale   : factor on q.k, > 0 and finite (usually 1/sqrt(D)).
  * Rows are rescaled when their running max grows by more than 8 in base-2
@@ -238,7 +237,7 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
  *              NULL for 1.0 (read by the kernel, so they may be produced by
  *              fa_quantize_fp8 on the same stream without a host sync).
  *   o        : [B, H, N, D] bfloat16; lse: [B, H, N] float.
- *   D        : 64 or 128.
+ *   D        : 64, 128 or 256.
  * Both products use fp8 MFMA, with the descales folded into the score scale
  * and the output. The probabilities are encoded as e4m3(p * 112) (p <= 4:
  * the rescale threshold is 2) for the P.V product, and the row sums that

@@ -58,7 +58,7 @@ def _fwd(**kw):
     (dict(scale=0.0), fa.FA_ERR_INVALID_ARG, "scale"),
     (dict(dtype=7), fa.FA_ERR_INVALID_ARG, "dtype"),
     (dict(D=96), fa.FA_ERR_UNSUPPORTED, "D=96"),
-    (dict(D=256, dtype=fa.FA_FP8_E4M3), fa.FA_ERR_UNSUPPORTED, "D=256"),
+    (dict(D=512, dtype=fa.FA_FP8_E4M3), fa.FA_ERR_UNSUPPORTED, "D=512"),
     (dict(N=1 << 24, D=128), fa.FA_ERR_INVALID_ARG, "2^31"),
 ])
 def test_fwd_validation(kw, status, msg):
@@ -76,7 +76,7 @@ def test_fwd_ex_threshold_validation():
 def test_fwd_fp8_validation():
     L = fa.lib()
     assert L.fa_fwd_fp8(P, P, P, P, P, 1, 1, 16, 128, 0, 0.1, P + 2, None, None, None) == fa.FA_ERR_INVALID_ARG
-    assert L.fa_fwd_fp8(P, P, P, P, P, 1, 1, 16, 256, 0, 0.1, None, None, None, None) == fa.FA_ERR_UNSUPPORTED
+    assert L.fa_fwd_fp8(P, P, P, P, P, 1, 1, 16, 192, 0, 0.1, None, None, None, None) == fa.FA_ERR_UNSUPPORTED
 
 
 def test_quantize_validation():

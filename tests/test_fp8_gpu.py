@@ -78,7 +78,7 @@ def _fp8_case(shape, causal, seed, rows=None):
     assert rel <= REL_FP8
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp8_small(D, causal):
     for i, N in enumerate([1, 5, 28, 29, 30, 31, 64, 65, 200, 1000]):
@@ -88,6 +88,12 @@ def test_fp8_small(D, causal):
 def test_fp8_long_context_workload_sampled():
     """B=1 H=32 N=32768 D=128 e4m3 causal: sampled rows of every head (plus bit-exact codes)."""
     w = inputs.WORKLOADS["long_fp8_causal"]
+    _fp8_case(w.shape, w.causal, w.seed, rows=sample_rows(w.N))
+
+
+def test_fp8_d256_workload_sampled():
+    """B=1 H=16 N=16384 D=256 e4m3 causal (two waves per SIMD): sampled rows of every head, bit-exact codes."""
+    w = inputs.WORKLOADS["fp8_d256_causal"]
     _fp8_case(w.shape, w.causal, w.seed, rows=sample_rows(w.N))
 
 
@@ -111,7 +117,8 @@ def _codes(rng, shape):
 # (H, Hkv, Nq, Nk, D, causal, window): grouped K/V heads, unequal lengths (causal aligned at the bottom
 # right), a sliding window, ragged tails on both sides and a query block longer than the keys
 GENERAL = [(4, 2, 200, 333, 64, True, -1), (4, 1, 333, 200, 128, True, -1), (8, 2, 257, 257, 128, True, 64),
-           (2, 2, 130, 515, 128, False, 100), (6, 3, 77, 1000, 64, False, -1), (4, 4, 600, 129, 128, True, 0)]
+           (2, 2, 130, 515, 128, False, 100), (6, 3, 77, 1000, 64, False, -1), (4, 4, 600, 129, 128, True, 0),
+           (4, 2, 300, 700, 256, True, -1), (2, 1, 129, 129, 256, True, 40)]
 
 
 @pytest.mark.parametrize("H,Hkv,Nq,Nk,D,causal,window", GENERAL)

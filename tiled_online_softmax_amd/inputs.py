@@ -124,6 +124,8 @@ WORKLOADS: Dict[str, Workload] = {
     # The backward at the largest head dimension: the large-head-dim workload's shape and values, causal.
     "bwd_d256_bf16": Workload("bwd_d256_bf16", 1, 8, 8192, 256, "bf16", True, "bwd", multiplier=0.5,
                               seed=SEED_BASE + 11),
+    # The e4m3 forward at the largest head dimension: causal, 16 heads of 16384 rows.
+    "fp8_d256_causal": Workload("fp8_d256_causal", 1, 16, 16384, 256, "fp8", True, "fwd", seed=SEED_BASE + 12),
     # Grouped-query attention (a NEXT-row extension): 32 query heads sharing 8 K/V heads.
     "gqa_causal_bf16": Workload("gqa_causal_bf16", 4, 32, 2048, 128, "bf16", True, "fwd+bwd", seed=SEED_BASE + 6,
                                 hkv=8),
