@@ -442,4 +442,10 @@ __device__ __forceinline__ int cvt_fp8x2(float a, float b, int old) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
 }
 
+// Float -> unsigned byte (rounded to nearest, clamped to [0, 255]) written
+// into byte `sel` of `old`; the other bytes are kept (v_cvt_pk_u8_f32).
+__device__ __forceinline__ unsigned cvt_u8(float a, unsigned sel, unsigned old) {
+  return __builtin_amdgcn_cvt_pk_u8_f32(a, sel, old);
+}
+
 }  // namespace fa

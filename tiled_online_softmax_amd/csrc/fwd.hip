@@ -42,15 +42,21 @@ struct BoolTag {
 //   * e4m3: both products run on the 32x32x64 fp8 MFMA. The descales fold
 //     into the score scale and the output; V^T operands are read with
 //     transposing 8-bit LDS reads (ds_read_b64_tr_b8); P is encoded as
-//     e4m3(p * 112), the exponentials taking log2 112 into their offset, so a
-//     row's reference max may trail its true max by up to 2 (base 2) before
-//     the accumulator must be rescaled (p <= 4 still fits e4m3's 448). e4m3
-//     keeps 3 significand bits, so an encoded probability is off by up to 2^-4
-//     of itself, and a row whose keys all sit in one or two tiles would carry
-//     that into O almost undiluted. On tiles that need masking (the causal
-//     diagonal, the ragged tail, a window start: all the keys of such short
-//     rows) P is therefore encoded as two e4m3 terms, the rounding and its
-//     residual, which multiply the same V^T operand: about 2^-8 relative error.
+//     e4m3(p * 112), the exponent offset by log2 112, so a row's reference
+//     max may trail its true max by up to 2 (base 2) before the accumulator
+//     must be rescaled (p <= 4 still fits e4m3's 448). The exponential and
+//     the encoding are one step, an emulated exponential with an e4m3 result
+//     (kCodeShift below): a fused multiply-add and a byte conversion per
+//     score, where the hardware exponential, a multiply-add and half a
+//     two-value conversion cost about three times as much issue time. e4m3
+//     keeps 3 significand bits, so an encoded probability is off by several
+//     percent of itself, and a row whose keys all sit in one or two tiles
+//     would carry that into O almost undiluted. On tiles that need masking
+//     (the causal diagonal, the ragged tail, a window start: all the keys of
+//     such short rows), and for rows that keep few keys, P is therefore
+//     encoded as two e4m3 terms: the code, and the rest of p * 112 (from the
+//     hardware exponential) rounded to nearest, which multiply the same V^T
+//     operand: well under 1% relative error.
 // The tile loop is unrolled by two so the stage base of every LDS read is an
 // immediate.
 // ---------------------------------------------------------------------------
@@ -58,6 +64,18 @@ struct BoolTag {
 // for p <= 2^kTauP8 = 4, which fixes the rescale threshold at kTauP8.
 constexpr float kTauP8 = 2.f;
 constexpr float kLog2P8 = 6.80735492205760410744f;  // log2(112)
+// Emulated exponential for unmasked e4m3 tiles. For t = log2(p * 112), the
+// e4m3 code of 2^t (normal range) is 8 (floor(t) + 7) + 8 (2^f - 1) rounded,
+// f = t - floor(t): bias 7, three significand bits. Replacing 2^f - 1 by its
+// chord f gives the code straight from t, round(8 t + 56 - shift); the chord
+// lies above the curve by up to 0.69 code units, and the shift 0.4566 makes
+// the decoded value's ratio to 2^t average 1 over a uniform f (its rms
+// deviation is 3.1%, against 2.6% for round-to-nearest). t <= log2 448 keeps
+// the code at most 126 (448); t below -7 gives a negative value, which the
+// byte conversion clamps to code 0.
+constexpr float kCodeShift = 0.4566f;
+// Rows keeping at most this many keys take the residual term on every tile.
+constexpr int kFewKeysP8 = 256;
 
 template <Elt E, int D_, int BN_, int NW_, int OCC_>
 struct FwdDCfg {
@@ -186,6 +204,10 @@ fwd_kernel(FwdParams P) {
   const KeyTiles<SPARSE, BN> ts(P, bh, kb, q0, q0 + C::BM);
   const int n_tiles = ts.n;
   const int hi_w = kb.hi(qw + 31);
+  // e4m3: rows that keep few keys (every row of this wave at most kFewKeysP8)
+  // average little of the encoding error away, so they take the residual term
+  // on every tile, not only on masked ones.
+  const bool few_keys = FP8 && hi_w - kb.lo(qw) < kFewKeysP8;
 
   if (n_tiles > 0) issue(ts.at_clamped(0) * BN, smem);
   // unconditional: a path that reached the tile loop with the Q loads pending
@@ -193,27 +215,40 @@ fwd_kernel(FwdParams P) {
   wait_vmem();
   __syncthreads();
 
-  // e4m3 P.V for one 64-key chunk kc. RESIDUAL = false: P (from the scores s,
-  // already p * 112) encoded as e4m3. RESIDUAL = true: a second pass for masked
-  // tiles that encodes what the first encoding rounded away,
-  // p * 112 - decode(e4m3(p * 112)), and adds its product with the same V^T
-  // operand. Both add their encoded row sums to l_acc.
-  auto pv_fp8 = [&](const f32x16 (&s)[NB], const char* vs, int kc, auto residual) __attribute__((always_inline)) {
-    constexpr bool RESIDUAL = decltype(residual)::value;
+  // e4m3 P of a 64-key tile, written into pb: the emulated exponential of the
+  // raw scores s, code = round(s * sc8 + c8) with sc8 = 8 sc and
+  // c8 = 8 neg_m + 56 - kCodeShift, one byte conversion per score (negative
+  // values, masked scores among them, clamp to code 0).
+  static_assert(!FP8 || BN == 64, "e4m3 tiles are one 64-key chunk (pb holds the chunk's codes)");
+  const float sc8 = 8.f * sc;
+  float c8 = 8.f * neg_m + (56.f - kCodeShift);
+  auto encode_p = [&](const f32x16 (&s)[NB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const f32x16& sb = s[2 * kc + (j >> 2)];
+      const f32x16& sb = s[j >> 2];
       const int o = (j & 3) * 4;
-      int w32 = cvt_fp8x2<false>(sb[o], sb[o + 1], pb[j]);
-      w32 = cvt_fp8x2<true>(sb[o + 2], sb[o + 3], w32);
-      if constexpr (RESIDUAL) {
-        const auto d01 = __builtin_amdgcn_cvt_pk_f32_fp8(w32, false);
-        const auto d23 = __builtin_amdgcn_cvt_pk_f32_fp8(w32, true);
-        w32 = cvt_fp8x2<false>(sb[o] - d01[0], sb[o + 1] - d01[1], w32);
-        w32 = cvt_fp8x2<true>(sb[o + 2] - d23[0], sb[o + 3] - d23[1], w32);
-      }
+      unsigned w32 = (unsigned)pb[j];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) w32 = cvt_u8(__builtin_fmaf(sb[o + u], sc8, c8), u, w32);
+      pb[j] = (int)w32;
+    }
+  };
+  // Masked tiles: a second term, what the codes in pb leave out of p * 112
+  // (the exact value from the exponential, p = s here), rounded to nearest.
+  auto encode_residual = [&](const f32x16 (&s)[NB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const f32x16& sb = s[j >> 2];
+      const int o = (j & 3) * 4;
+      const auto d01 = __builtin_amdgcn_cvt_pk_f32_fp8(pb[j], false);
+      const auto d23 = __builtin_amdgcn_cvt_pk_f32_fp8(pb[j], true);
+      int w32 = cvt_fp8x2<false>(sb[o] - d01[0], sb[o + 1] - d01[1], pb[j]);
+      w32 = cvt_fp8x2<true>(sb[o + 2] - d23[0], sb[o + 3] - d23[1], w32);
       pb[j] = w32;
     }
+  };
+  // O^T += V^T P^T for chunk kc with the P in pb; its row sums go to l_acc.
+  auto mul_pv = [&](const char* vs, int kc) __attribute__((always_inline)) {
     l_acc = mfma_fp8_16(ones_sel, pb, l_acc);
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
@@ -295,26 +330,32 @@ fwd_kernel(FwdParams P) {
         m_ref = m_new;
         // a row that has kept no key yet (m_ref = -inf, only under a window) gets p = 2^-inf = 0
         neg_m = (m_ref == -INFINITY ? 0.f : -m_ref) + (FP8 ? kLog2P8 : 0.f);
-        if constexpr (FP8)
+        if constexpr (FP8) {
           l_acc *= alpha;
-        else
+          c8 = 8.f * neg_m + (56.f - kCodeShift);
+        } else {
           l_part *= alpha;
+        }
 #pragma unroll
         for (int e = 0; e < NE; ++e) acc[e] *= alpha;
       }
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) s[b][v] = fast_exp2(__builtin_fmaf(s[b][v], sc, neg_m));
       // ---- O^T += V^T P^T ----
       if constexpr (FP8) {
+        encode_p(s);
+        mul_pv(vs, 0);
+        if (masked || few_keys) {
 #pragma unroll
-        for (int kc = 0; kc < BN / 64; ++kc) pv_fp8(s, vs, kc, BoolTag<false>{});
-        if (masked) {
+          for (int b = 0; b < NB; ++b)
 #pragma unroll
-          for (int kc = 0; kc < BN / 64; ++kc) pv_fp8(s, vs, kc, BoolTag<true>{});
+            for (int v = 0; v < 16; ++v) s[b][v] = fast_exp2(__builtin_fmaf(s[b][v], sc, neg_m));
+          encode_residual(s);
+          mul_pv(vs, 0);
         }
       } else {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) s[b][v] = fast_exp2(__builtin_fmaf(s[b][v], sc, neg_m));
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
