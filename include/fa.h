@@ -253,6 +253,30 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                const float* v_descale, void* stream);
 
 /*
+ * FP8 forward with per-tensor scales on the general layouts: fa_fwd_general's
+ * grouped K/V heads, query and key lengths and window (fa_fwd_fp8_general),
+ * and fa_fwd_varlen's packed sequences (fa_fwd_fp8_varlen), with e4m3 codes
+ * and the descale pointers of fa_fwd_fp8 (grouped-query attention and
+ * prefill with a cached prefix are how the FP8 forward of the "r/mlscaling"
+ * page's FA3 bullet is used in serving). O is bfloat16. Arguments, layouts
+ * and errors as for those calls and fa_fwd_fp8; fa_fwd_fp8 is
+ * fa_fwd_fp8_general with Hkv = H, Nq = Nk = N and window = -1.
+ */
+int fa_fwd_fp8_general(const void* q, const void* k, const void* v, void* o,
+                       float* lse, int B, int H, int Hkv, int Nq, int Nk, int D,
+                       int causal, int window, float scale,
+                       const float* q_descale, const float* k_descale,
+                       const float* v_descale, void* stream);
+int fa_fwd_fp8_varlen(const void* q, const void* k, const void* v, void* o,
+                      float* lse, const int* cu_seqlens_q,
+                      const int* cu_seqlens_k, int B, int H, int Hkv,
+                      int total_q, int total_k, int max_seqlen_q,
+                      int max_seqlen_k, int D, int causal, int window,
+                      float scale, const float* q_descale,
+                      const float* k_descale, const float* v_descale,
+                      void* stream);
+
+/*
  * Per-tensor FP8 quantisation (the operand preparation of the FP8 forward):
  *   amax    = max |x_i| over all n elements,
  *   codes_i = e4m3 round-to-nearest-even of x_i * (448 / amax) (float32

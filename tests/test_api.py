@@ -79,6 +79,25 @@ def test_fwd_fp8_validation():
     assert L.fa_fwd_fp8(P, P, P, P, P, 1, 1, 16, 192, 0, 0.1, None, None, None, None) == fa.FA_ERR_UNSUPPORTED
 
 
+def test_fwd_fp8_general_and_varlen_validation():
+    L = fa.lib()
+    # fa_fwd_fp8_general(q, k, v, o, lse, B, H, Hkv, Nq, Nk, D, causal, window, scale, q_ds, k_ds, v_ds, stream)
+    gen = lambda H=8, Hkv=2, Nq=16, Nk=32, D=128, window=-1, qd=None: L.fa_fwd_fp8_general(
+        P, P, P, P, P, 1, H, Hkv, Nq, Nk, D, 1, window, 0.1, qd, None, None, None)
+    assert gen(qd=P + 2) == fa.FA_ERR_INVALID_ARG and "descale" in fa.last_error()
+    assert gen(Hkv=3) == fa.FA_ERR_INVALID_ARG and "divide" in fa.last_error()
+    assert gen(Nk=0) == fa.FA_ERR_INVALID_ARG
+    assert gen(window=-2) == fa.FA_ERR_INVALID_ARG
+    assert gen(D=96) == fa.FA_ERR_UNSUPPORTED and "D=96" in fa.last_error()
+    # fa_fwd_fp8_varlen(q, k, v, o, lse, cu_q, cu_k, B, H, Hkv, Tq, Tk, max_q, max_k, D, causal, window, scale, ...)
+    var = lambda cu=P, Tq=100, D=64, vd=None: L.fa_fwd_fp8_varlen(
+        P, P, P, P, P, cu, P, 2, 4, 2, Tq, 100, 64, 64, D, 1, -1, 0.1, None, None, vd, None)
+    assert var(cu=None) == fa.FA_ERR_INVALID_ARG and "cu_seqlens_q" in fa.last_error()
+    assert var(vd=P + 1) == fa.FA_ERR_INVALID_ARG and "descale" in fa.last_error()
+    assert var(Tq=0) == fa.FA_ERR_INVALID_ARG
+    assert var(D=80) == fa.FA_ERR_UNSUPPORTED
+
+
 def test_quantize_validation():
     L = fa.lib()
     assert L.fa_quantize_fp8(P, 0, P, P, None) == fa.FA_ERR_INVALID_ARG

@@ -174,3 +174,58 @@ def test_fp8_varlen():
         eo, el = max_abs(og, o_ref), max_abs(lg[live], lse_ref[live])
         print(f"[fp8 varlen causal={causal} window={window}] O {eo:.3e} lse {el:.3e}", flush=True)
         assert eo <= TOL_FP8 and el <= TOL_FP8
+
+
+def _quantized(x: np.ndarray):
+    """GPU quantisation of float32 draws (codes, descale) and the oracle's dequantisation of the same draws."""
+    codes, desc = fa.quantize_fp8(f32_tensor(x))
+    return codes, desc, codecs.dequantize(*codecs.quantize_per_tensor(x))
+
+
+@pytest.mark.parametrize("H,Hkv,Nq,Nk,D,causal,window", [(8, 2, 300, 1100, 128, True, -1),
+                                                          (4, 1, 129, 129, 64, True, 50),
+                                                          (6, 3, 200, 77, 256, False, -1)])
+def test_fp8_general_per_tensor_scales(H, Hkv, Nq, Nk, D, causal, window):
+    """fa_fwd_fp8_general: grouped K/V heads, unequal lengths and a window with per-tensor descales, against the
+    oracle on the dequantised values (the GPU codes are bit-exact with the oracle codec, tested above)."""
+    rng = np.random.default_rng(8000 + H + Nq + Nk + D)
+    xs = [(rng.standard_normal(s) * m).astype(np.float32)
+          for s, m in (((2, H, Nq, D), 1.5), ((2, Hkv, Nk, D), 0.7), ((2, Hkv, Nk, D), 3.0))]
+    (qc, qd, qr), (kc, kd, kr), (vc, vd, vr) = (_quantized(x) for x in xs)
+    scale = 1 / math.sqrt(D)
+    o, lse = fa.fwd_fp8(qc, kc, vc, causal=causal, scale=scale, q_descale=qd, k_descale=kd, v_descale=vd,
+                        window=None if window < 0 else window)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = attention.forward(qr, kr, vr, causal, scale, window=window)
+    live = lse_ref != -np.inf
+    og, lg = to_f64(o), to_f64(lse)
+    assert np.all(og[~live] == 0) and np.all(lg[~live] == -np.inf)
+    # O carries v's scale (|v| up to 3 x 4.5 here): the bound scales with the value range
+    eo, el = max_abs(og, o_ref) / 3.0, max_abs(lg[live], lse_ref[live])
+    print(f"[fp8 general scaled H{H}/{Hkv} Nq{Nq} Nk{Nk} D{D}] O/3 {eo:.3e} lse {el:.3e}", flush=True)
+    assert eo <= TOL_FP8 and el <= TOL_FP8
+
+
+def test_fp8_varlen_per_tensor_scales():
+    """fa_fwd_fp8_varlen: packed sequences (an empty one, a one-row one, ragged ones), grouped heads, descales.
+    q and k are scaled by 2 and 1/2, so the descales differ from 1 while the scores keep the N(0,1) spread the
+    tolerance is stated for."""
+    rng = np.random.default_rng(8100)
+    lq, lk = [77, 0, 1, 300, 129], [300, 5, 1, 300, 64]
+    cu_q, cu_k = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    H, Hkv, D = 8, 2, 128
+    xs = [(rng.standard_normal((t, h, D)) * m).astype(np.float32)
+          for t, h, m in ((cu_q[-1], H, 2.0), (cu_k[-1], Hkv, 0.5), (cu_k[-1], Hkv, 0.5))]
+    (qc, qd, qr), (kc, kd, kr), (vc, vd, vr) = (_quantized(x) for x in xs)
+    cq, ck = (torch.from_numpy(c.astype(np.int32)).to(DEV) for c in (cu_q, cu_k))
+    for causal, window in ((True, -1), (False, 40)):
+        o, lse = fa.fwd_fp8_varlen(qc, kc, vc, cq, ck, max(lq), max(lk), causal=causal, scale=0.1,
+                                   window=None if window < 0 else window, q_descale=qd, k_descale=kd, v_descale=vd)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = attention.forward_varlen(qr, kr, vr, cu_q, cu_k, causal, 0.1, window=window)
+        live = lse_ref != -np.inf
+        og, lg = to_f64(o), to_f64(lse)
+        assert np.all(lg[~live] == -np.inf) and np.all(og.transpose(1, 0, 2)[~live] == 0)
+        eo, el = max_abs(og, o_ref) / 0.5, max_abs(lg[live], lse_ref[live])
+        print(f"[fp8 varlen scaled causal={causal} window={window}] O/0.5 {eo:.3e} lse {el:.3e}", flush=True)
+        assert eo <= TOL_FP8 and el <= TOL_FP8

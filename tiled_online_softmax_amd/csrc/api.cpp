@@ -192,6 +192,13 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   return hip_status(fa::fwd_dispatch(e, D, p, B, H, reinterpret_cast<hipStream_t>(stream)), "fa_fwd launch");
 }
 
+// Descale pointers are optional (NULL reads as 1.0) and read by the kernel as floats.
+int check_descales(const float* q_descale, const float* k_descale, const float* v_descale) {
+  for (const float* d : {q_descale, k_descale, v_descale})
+    if (d && (reinterpret_cast<uintptr_t>(d) & 3u)) return fail(FA_ERR_INVALID_ARG, "descale pointer not 4-byte aligned");
+  return FA_OK;
+}
+
 Layout strides_from(const long long* st, int n_tensors) {
   Layout L{};
   fa::Strides* t[] = {&L.q, &L.k, &L.v, &L.o, &L.dO, &L.dq, &L.dk, &L.dv};
@@ -288,10 +295,27 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, 
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int D,
                int causal, float scale, const float* q_descale, const float* k_descale, const float* v_descale,
                void* stream) {
-  for (const float* d : {q_descale, k_descale, v_descale})
-    if (d && (reinterpret_cast<uintptr_t>(d) & 3u)) return fail(FA_ERR_INVALID_ARG, "descale pointer not 4-byte aligned");
-  return fwd_impl(q, k, v, o, lse, B, H, H, N, N, D, causal, -1, scale, FA_FP8_E4M3, 0.0f, q_descale, k_descale,
-                  v_descale, contiguous(H, H, N, N, D), stream);
+  return fa_fwd_fp8_general(q, k, v, o, lse, B, H, H, N, N, D, causal, -1, scale, q_descale, k_descale, v_descale,
+                            stream);
+}
+
+int fa_fwd_fp8_general(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
+                       int Nq, int Nk, int D, int causal, int window, float scale, const float* q_descale,
+                       const float* k_descale, const float* v_descale, void* stream) {
+  if (int s = check_descales(q_descale, k_descale, v_descale)) return s;
+  return fwd_impl(q, k, v, o, lse, B, H, Hkv, Nq, Nk, D, causal, window, scale, FA_FP8_E4M3, 0.0f, q_descale,
+                  k_descale, v_descale, contiguous(H, Hkv, Nq, Nk, D), stream);
+}
+
+int fa_fwd_fp8_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_seqlens_q,
+                      const int* cu_seqlens_k, int B, int H, int Hkv, int total_q, int total_k, int max_seqlen_q,
+                      int max_seqlen_k, int D, int causal, int window, float scale, const float* q_descale,
+                      const float* k_descale, const float* v_descale, void* stream) {
+  if (!cu_seqlens_q) return fail(FA_ERR_INVALID_ARG, "cu_seqlens_q is NULL");
+  if (int s = check_descales(q_descale, k_descale, v_descale)) return s;
+  return fwd_impl(q, k, v, o, lse, B, H, Hkv, max_seqlen_q, max_seqlen_k, D, causal, window, scale, FA_FP8_E4M3,
+                  0.0f, q_descale, k_descale, v_descale,
+                  packed(H, Hkv, D, cu_seqlens_q, cu_seqlens_k, total_q, total_k), stream);
 }
 
 int fa_quantize_fp8(const float* x, size_t n, void* codes, float* descale, void* stream) {

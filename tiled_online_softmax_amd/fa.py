@@ -24,7 +24,8 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0,
 FA_BWD_ATOMIC, FA_BWD_DETERMINISTIC = 0, 1
 
 EXPORTED = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_general", "fa_fwd_strided", "fa_fwd_varlen", "fa_block_lists",
-            "fa_fwd_sparse", "fa_fwd_ex", "fa_fwd_fp8", "fa_quantize_fp8", "fa_bwd_workspace_size", "fa_bwd",
+            "fa_fwd_sparse", "fa_fwd_ex", "fa_fwd_fp8", "fa_fwd_fp8_general", "fa_fwd_fp8_varlen", "fa_quantize_fp8",
+            "fa_bwd_workspace_size", "fa_bwd",
             "fa_bwd_gqa", "fa_bwd_general", "fa_bwd_strided", "fa_bwd_sparse", "fa_bwd_varlen", "fa_bwd_dkdv",
             "fa_bwd_noalloc", "fa_status_string", "fa_last_error")
 BLOCK = 128  # rows and columns of a block of a block-sparse mask
@@ -56,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd_sparse.argtypes = [_vp] * 5 + [_i] * 8 + [_f, _i, _vp, _vp, _vp]
         L.fa_fwd_ex.argtypes = [_vp] * 5 + [_i] * 5 + [_f, _i, _f, _vp]
         L.fa_fwd_fp8.argtypes = [_vp] * 5 + [_i] * 5 + [_f] + [_vp] * 3 + [_vp]
+        L.fa_fwd_fp8_general.argtypes = [_vp] * 5 + [_i] * 8 + [_f] + [_vp] * 3 + [_vp]
+        L.fa_fwd_fp8_varlen.argtypes = [_vp] * 7 + [_i] * 10 + [_f] + [_vp] * 3 + [_vp]
         L.fa_quantize_fp8.argtypes = [_vp, _sz, _vp, _vp, _vp]
         L.fa_bwd_workspace_size.argtypes = [_i] * 6
         L.fa_bwd_workspace_size.restype = _sz
@@ -72,7 +75,8 @@ def lib() -> ctypes.CDLL:
         L.fa_last_error.argtypes = []
         L.fa_last_error.restype = ctypes.c_char_p
         for name in ("fa_fwd", "fa_fwd_gqa", "fa_fwd_general", "fa_fwd_strided", "fa_fwd_varlen", "fa_block_lists",
-                     "fa_fwd_sparse", "fa_fwd_ex", "fa_fwd_fp8", "fa_quantize_fp8", "fa_bwd", "fa_bwd_gqa",
+                     "fa_fwd_sparse", "fa_fwd_ex", "fa_fwd_fp8", "fa_fwd_fp8_general", "fa_fwd_fp8_varlen",
+                     "fa_quantize_fp8", "fa_bwd", "fa_bwd_gqa",
                      "fa_bwd_general", "fa_bwd_strided", "fa_bwd_sparse", "fa_bwd_varlen", "fa_bwd_dkdv",
                      "fa_bwd_noalloc"):
             getattr(L, name).restype = _i
@@ -253,12 +257,16 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
 def fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False, scale: Optional[float] = None,
             q_descale: Optional[torch.Tensor] = None, k_descale: Optional[torch.Tensor] = None,
             v_descale: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-            lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """FP8 (e4m3 codes, uint8 or float8_e4m3fn tensors) forward with per-tensor descales (1-element device tensors)."""
-    _check_qkv(q, k, v)
-    if q.dtype not in (torch.uint8, torch.float8_e4m3fn):
-        raise ValueError("fwd_fp8 takes e4m3 codes (uint8 or float8_e4m3fn tensors)")
+            lse: Optional[torch.Tensor] = None, window: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """FP8 (e4m3 codes, uint8 or float8_e4m3fn tensors) forward with per-tensor descales (1-element device tensors).
+
+    k, v may have fewer heads (grouped-query) and another length than q (causal aligned at the bottom right), and
+    `window` (>= 0) keeps only the keys from i + Nk - Nq - window on (fa_fwd_fp8_general); contiguous tensors.
+    """
+    _check_qkv(q, kv=(k, v), same_len=False)
+    _check_fp8(q)
     B, H, N, D = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
@@ -266,16 +274,51 @@ def fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = Fa
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     _check_like(out, q.shape, torch.bfloat16, q.device, "out")
     _check_like(lse, (B, H, N), torch.float32, q.device, "lse")
+    d = [_descale_ptr(t, q) for t in (q_descale, k_descale, v_descale)]
+    if Hkv == H and Nk == N and window is None:
+        _check(lib().fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, D,
+                                int(causal), scale, *d, _stream(q)))
+    else:
+        _check(lib().fa_fwd_fp8_general(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B,
+                                        H, Hkv, N, Nk, D, int(causal), -1 if window is None else int(window), scale,
+                                        *d, _stream(q)))
+    return out, lse
 
-    def ptr(t):
-        if t is None:
-            return None
-        if t.dtype != torch.float32 or t.device != q.device or t.numel() < 1:
-            raise ValueError("descales must be float32 tensors on q's device with one element")
-        return t.data_ptr()
 
-    _check(lib().fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, D,
-                            int(causal), scale, ptr(q_descale), ptr(k_descale), ptr(v_descale), _stream(q)))
+def _check_fp8(q: torch.Tensor):
+    if q.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise ValueError("the FP8 forward takes e4m3 codes (uint8 or float8_e4m3fn tensors)")
+
+
+def _descale_ptr(t: Optional[torch.Tensor], q: torch.Tensor):
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or t.device != q.device or t.numel() < 1:
+        raise ValueError("descales must be float32 tensors on q's device with one element")
+    return t.data_ptr()
+
+
+@_on_device
+def fwd_fp8_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int, causal: bool = False,
+                   scale: Optional[float] = None, window: Optional[int] = None, q_descale=None, k_descale=None,
+                   v_descale=None, out=None, lse=None):
+    """Packed variable-length FP8 forward (fa_fwd_fp8_varlen): e4m3 codes q [total_q, H, D], k, v [total_k, Hkv, D],
+    per-tensor descales as in fwd_fp8. Returns (O bf16 [total_q, H, D], lse [H, total_q])."""
+    _check_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    _check_fp8(q)
+    Tq, H, D = q.shape
+    Tk, Hkv = k.shape[0], k.shape[1]
+    B = cu_seqlens_q.numel() - 1
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) if out is None else out
+    lse = torch.empty((H, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_like(out, q.shape, torch.bfloat16, q.device, "out")
+    _check_like(lse, (H, Tq), torch.float32, q.device, "lse")
+    d = [_descale_ptr(t, q) for t in (q_descale, k_descale, v_descale)]
+    _check(lib().fa_fwd_fp8_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                   cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H, Hkv, Tq, Tk,
+                                   int(max_seqlen_q), int(max_seqlen_k), D, int(causal),
+                                   -1 if window is None else int(window), scale, *d, _stream(q)))
     return out, lse
 
 
