@@ -80,6 +80,9 @@ enum { FA_BWD_ATOMIC = 0, FA_BWD_DETERMINISTIC = 1 };
  *   scale   : factor on q.k, > 0 and finite (usually 1/sqrt(D)).
  * Rows are rescaled when their running max grows by more than 8 in base-2
  * units (FA_FP8_E4M3: by more than 2), which is exact in exact arithmetic.
+ * Inputs must be finite: a NaN or infinite element gives undefined rows (the
+ * e4m3 forward, for one, encodes a NaN score as probability 0 on most tiles
+ * rather than propagating it).
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int D, int causal, float scale, int dtype,
