@@ -135,9 +135,9 @@ fwd_kernel(FwdParams P) {
   if constexpr (FP8) {
     // descales fold into the score scale and the output; P is encoded as
     // e4m3(p * 112), which needs p <= 4, hence the threshold kTauP8 = 2.
-    // The exponent is offset by log2 112, so the exponentials yield p * 112
-    // directly; the float32 row sum then also carries the factor, which
-    // cancels in O and is taken out of lse.
+    // The exponent is offset by log2 112, so the codes (and, on masked
+    // tiles, the exponentials) stand for p * 112 directly; the row sums then
+    // also carry the factor, which cancels in O and is taken out of lse.
     const float dq = P.q_descale ? *P.q_descale : 1.f;
     const float dk = P.k_descale ? *P.k_descale : 1.f;
     const float dv = P.v_descale ? *P.v_descale : 1.f;
@@ -186,10 +186,10 @@ fwd_kernel(FwdParams P) {
   // weights P.V used, in all four accumulator entries.
   f32x4 l_acc = {0.f, 0.f, 0.f, 0.f};
   i32x8 ones_sel;
-  // e4m3 P operand. Each word is written by two half-word packs, the first of
-  // which keeps the other half of its `old` operand: passing the previous
-  // tile's word there (overwritten anyway) keeps the words in place without
-  // zeroing moves.
+  // e4m3 P operand. Each word is written byte by byte (or, for the residual
+  // term, by two half-word packs), each conversion keeping the rest of its
+  // `old` operand: passing the previous tile's word there (overwritten
+  // anyway) keeps the words in place without zeroing moves.
   i32x8 pb = {};
   if constexpr (FP8) {
     const int v = ((lane >> 2) & 1) == ((lane >> 4) & 1) ? 0x38383838 : 0;  // e4m3 1.0 = 0x38
@@ -233,8 +233,9 @@ fwd_kernel(FwdParams P) {
       pb[j] = (int)w32;
     }
   };
-  // Masked tiles: a second term, what the codes in pb leave out of p * 112
-  // (the exact value from the exponential, p = s here), rounded to nearest.
+  // Masked tiles and rows with few keys: a second term, what the codes in pb
+  // leave out of p * 112 (the hardware exponential's value, in s here),
+  // rounded to nearest.
   auto encode_residual = [&](const f32x16 (&s)[NB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
