@@ -155,11 +155,12 @@ def test_all_true_mask_equals_dense(causal):
     assert all(torch.equal(a, b) for a, b in zip(g, g_d))
 
 
-def test_sparse_fp8_forward_runs_the_listed_blocks():
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_sparse_fp8_forward_runs_the_listed_blocks(D):
     """The fp8 forward takes the same lists: with unit descales it matches the oracle on decoded codes."""
     from oracle import codecs
-    B, H, N, D = 1, 2, 640, 128
-    rng = np.random.default_rng(7700)
+    B, H, N = 1, 2, 640
+    rng = np.random.default_rng(7700 + D)
     codes = [codecs.f64_to_e4m3(rng.standard_normal((B, H, N, D))) for _ in range(3)]
     qd, kd, vd = (torch.from_numpy(c).to(DEV) for c in codes)
     m = _mask(B, H, N, N, 0.5, 7701)
