@@ -229,3 +229,16 @@ def test_fp8_varlen_per_tensor_scales():
         eo, el = max_abs(og, o_ref) / 0.5, max_abs(lg[live], lse_ref[live])
         print(f"[fp8 varlen scaled causal={causal} window={window}] O/0.5 {eo:.3e} lse {el:.3e}", flush=True)
         assert eo <= TOL_FP8 and el <= TOL_FP8
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_fp8_forward_is_deterministic(D):
+    """Ten e4m3 forwards give bitwise-identical outputs (an LDS double-buffer race would show here)."""
+    rng = np.random.default_rng(8200 + D)
+    _, qd = _codes(rng, (2, 4, 1000, D))
+    _, kd = _codes(rng, (2, 4, 1000, D))
+    _, vd = _codes(rng, (2, 4, 1000, D))
+    o0, l0 = fa.fwd(qd, kd, vd, causal=True)
+    for _ in range(9):
+        o, l = fa.fwd(qd, kd, vd, causal=True)
+        assert torch.equal(o, o0) and torch.equal(l, l0)
