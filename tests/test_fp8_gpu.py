@@ -153,26 +153,27 @@ def test_fp8_strided_views():
     assert max_abs(to_f64(o), o_ref) <= TOL_FP8 and max_abs(to_f64(lse), lse_ref) <= TOL_FP8
 
 
-def test_fp8_varlen():
+@pytest.mark.parametrize("D", [64, 256])
+def test_fp8_varlen(D):
     """The packed variable-length forward on e4m3 codes: empty, one-row and ragged sequences, grouped heads."""
-    rng = np.random.default_rng(7900)
+    rng = np.random.default_rng(7900 + D)
     lq, lk = [0, 1, 130, 77, 300], [5, 1, 200, 0, 300]
     cu_q, cu_k = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
-    H, Hkv, D = 4, 2, 64
+    H, Hkv = 4, 2
     (qc, qd), (kc, kd), (vc, vd) = (_codes(rng, (t, h, D)) for t, h in ((cu_q[-1], H), (cu_k[-1], Hkv),
                                                                           (cu_k[-1], Hkv)))
     cq, ck = (torch.from_numpy(c.astype(np.int32)).to(DEV) for c in (cu_q, cu_k))
     for causal, window in ((False, -1), (True, -1), (True, 50)):
-        o, lse = fa.fwd_varlen(qd, kd, vd, cq, ck, max(lq), max(lk), causal=causal, scale=0.125,
+        o, lse = fa.fwd_varlen(qd, kd, vd, cq, ck, max(lq), max(lk), causal=causal, scale=1 / math.sqrt(D),
                                window=None if window < 0 else window)
         torch.cuda.synchronize()
         o_ref, lse_ref = attention.forward_varlen(*(codecs.e4m3_to_f64(c) for c in (qc, kc, vc)), cu_q, cu_k,
-                                                  causal, 0.125, window=window)
+                                                  causal, 1 / math.sqrt(D), window=window)
         live = lse_ref != -np.inf
         og, lg = to_f64(o), to_f64(lse)
         assert np.all(lg[~live] == -np.inf) and np.all(og.transpose(1, 0, 2)[~live] == 0)
         eo, el = max_abs(og, o_ref), max_abs(lg[live], lse_ref[live])
-        print(f"[fp8 varlen causal={causal} window={window}] O {eo:.3e} lse {el:.3e}", flush=True)
+        print(f"[fp8 varlen D{D} causal={causal} window={window}] O {eo:.3e} lse {el:.3e}", flush=True)
         assert eo <= TOL_FP8 and el <= TOL_FP8
 
 
