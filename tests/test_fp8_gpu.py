@@ -139,17 +139,19 @@ def test_fp8_general_layouts(H, Hkv, Nq, Nk, D, causal, window):
     assert eo <= TOL_FP8 and el <= TOL_FP8
 
 
-def test_fp8_strided_views():
+@pytest.mark.parametrize("window", [-1, 150])
+def test_fp8_strided_views(window):
     """The e4m3 forward on [B, N, H, D] storage seen as [B, H, N, D] views (fa_fwd_strided), grouped K/V heads."""
-    rng = np.random.default_rng(7850)
+    rng = np.random.default_rng(7850 + window)
     B, H, Hkv, Nq, Nk, D = 2, 4, 2, 190, 300, 128
     (qc, qd), (kc, kd), (vc, vd) = (_codes(rng, (B, n, h, D)) for h, n in ((H, Nq), (Hkv, Nk), (Hkv, Nk)))
     o = torch.empty((B, Nq, H, D), dtype=torch.bfloat16, device=DEV).transpose(1, 2)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=DEV)
-    fa.fwd(qd.transpose(1, 2), kd.transpose(1, 2), vd.transpose(1, 2), causal=True, scale=0.1, out=o, lse=lse)
+    fa.fwd(qd.transpose(1, 2), kd.transpose(1, 2), vd.transpose(1, 2), causal=True, scale=0.1, out=o, lse=lse,
+           window=None if window < 0 else window)
     torch.cuda.synchronize()
     vals = [codecs.e4m3_to_f64(c).transpose(0, 2, 1, 3) for c in (qc, kc, vc)]
-    o_ref, lse_ref = attention.forward(*vals, True, 0.1)
+    o_ref, lse_ref = attention.forward(*vals, True, 0.1, window=window)
     assert max_abs(to_f64(o), o_ref) <= TOL_FP8 and max_abs(to_f64(lse), lse_ref) <= TOL_FP8
 
 

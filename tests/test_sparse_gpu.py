@@ -155,26 +155,29 @@ def test_all_true_mask_equals_dense(causal):
     assert all(torch.equal(a, b) for a, b in zip(g, g_d))
 
 
-@pytest.mark.parametrize("D", [64, 128, 256])
-def test_sparse_fp8_forward_runs_the_listed_blocks(D):
-    """The fp8 forward takes the same lists: with unit descales it matches the oracle on decoded codes."""
+@pytest.mark.parametrize("D,window", [(64, -1), (128, -1), (256, -1), (128, 200)])
+def test_sparse_fp8_forward_runs_the_listed_blocks(D, window):
+    """The fp8 forward takes the same lists (and a window): with unit descales it matches the oracle on decoded
+    codes."""
     from oracle import codecs
     B, H, N = 1, 2, 640
     rng = np.random.default_rng(7700 + D)
     codes = [codecs.f64_to_e4m3(rng.standard_normal((B, H, N, D))) for _ in range(3)]
     qd, kd, vd = (torch.from_numpy(c).to(DEV) for c in codes)
     m = _mask(B, H, N, N, 0.5, 7701)
-    bl = fa.block_lists(torch.from_numpy(m).to(DEV), N, N, True)
+    bl = fa.block_lists(torch.from_numpy(m).to(DEV), N, N, True, None if window < 0 else window)
     o = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=DEV)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=DEV)
     L = fa.lib()
     fa._check(L.fa_fwd_sparse(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, H, N,
-                              N, D, 1, -1, 1 / math.sqrt(D), fa.FA_FP8_E4M3, bl.kv_count.data_ptr(),
+                              N, D, 1, window, 1 / math.sqrt(D), fa.FA_FP8_E4M3, bl.kv_count.data_ptr(),
                               bl.kv_index.data_ptr(), None))
     torch.cuda.synchronize()
     vals = [codecs.e4m3_to_f64(c) for c in codes]
-    o_ref, lse_ref = attention.forward(vals[0], vals[1], vals[2], True, 1 / math.sqrt(D), block_mask=m)
+    o_ref, lse_ref = attention.forward(vals[0], vals[1], vals[2], True, 1 / math.sqrt(D), window=window,
+                                       block_mask=m)
     live = lse_ref != -np.inf
+    assert np.all(to_f64(lse)[~live] == -np.inf) and np.all(to_f64(o)[~live] == 0)
     assert max_abs(to_f64(o), o_ref) <= 6e-2 and max_abs(to_f64(lse)[live], lse_ref[live]) <= 6e-2
 
 
