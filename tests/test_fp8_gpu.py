@@ -245,3 +245,19 @@ def test_fp8_forward_is_deterministic(D):
     for _ in range(9):
         o, l = fa.fwd(qd, kd, vd, causal=True)
         assert torch.equal(o, o0) and torch.equal(l, l0)
+
+
+def test_fp8_scores_twice_as_spread():
+    """Peakier rows than N(0,1) scores give (q drawn with standard deviation 2): the e4m3 forward, whose encoding
+    error is diluted less when fewer keys carry the row, still meets the tolerance (2048 causal rows, most of
+    them past the 256 keys below which every tile takes the residual term)."""
+    rng = np.random.default_rng(8300)
+    qc = codecs.f64_to_e4m3(rng.standard_normal((1, 4, 2048, 128)) * 2.0)
+    kc, vc = (codecs.f64_to_e4m3(rng.standard_normal((1, 4, 2048, 128))) for _ in range(2))
+    t = [torch.from_numpy(c).to(DEV) for c in (qc, kc, vc)]
+    o, lse = fa.fwd(t[0], t[1], t[2], causal=True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = attention.forward(*(codecs.e4m3_to_f64(c) for c in (qc, kc, vc)), True, 1 / math.sqrt(128))
+    eo, el = max_abs(to_f64(o), o_ref), max_abs(to_f64(lse), lse_ref)
+    print(f"[fp8 spread x2] O {eo:.3e} lse {el:.3e}", flush=True)
+    assert eo <= TOL_FP8 and el <= TOL_FP8
